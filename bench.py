@@ -1,0 +1,248 @@
+"""Benchmark of one decode step of one layer: KV append + paged decode attention.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config gqa_bf16] [--partition 0]
+
+A step is the whole hot path over one batch: the append of one new token per sequence
+(``pkv_kv_cache_append``) followed by paged decode attention over every context including
+that token (``pkv_paged_attn_decode``), with all inputs resident in HBM.  The default
+workload is the Llama-3-70B-shaped GQA decode (batch 256, 64 query / 8 KV heads, head dim
+128, bf16, lognormal context lengths with median 512 clipped to [16, 8192], seed 0).
+
+Prints one JSON line: KV GB/s of the step (bytes of K and V the decode reads per step over
+the step time), the fraction of MI355X's 8 TB/s HBM peak, attention-only decode tokens/s
+at the 80-layer 70B shape, a roofline record for the decode launch (timed with HIP events
+on its stream) and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+LAYERS_70B = 80        # layers of the 70B model whose shape the default workload has
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, part, num_parts_of):
+    """Bytes the decode launch must move (K/V read once, q read, out written, tables and
+    lengths read, split partials written and read back)."""
+    sp = w.spec
+    e = {"float32": 4, "float16": 2, "bfloat16": 2}[sp.dtype]
+    lens = [int(L) + 1 for L in w.context_lens]
+    kv = sum(lens) * sp.num_kv_heads * sp.head_dim * 2 * e
+    qo = 2 * sp.num_seqs * sp.num_q_heads * sp.head_dim * e
+    tables = 4 * sum(-(-L // 16) for L in lens) + 4 * sp.num_seqs
+    partials = 0
+    for L in lens:
+        P = num_parts_of(L, part)
+        if P > 1:
+            partials += 2 * P * sp.num_q_heads * (sp.head_dim + 2) * 4
+    return kv, kv + qo + tables + partials
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The fp64 oracle on the host cores over a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+
+    sp = w.spec
+    e = {"float32": 4, "float16": 2, "bfloat16": 2}[sp.dtype]
+    order = list(range(sp.num_seqs))
+    done_bytes, seqs, t_total = 0, 0, 0.0
+    for s in order:
+        k, v = w.seq_kv_after_append(s)
+        t0 = time.perf_counter()
+        oracle.decode_attention(w.q[s:s + 1], [k], [v], w.scale)
+        t_total += time.perf_counter() - t0
+        done_bytes += k.shape[0] * sp.num_kv_heads * sp.head_dim * 2 * e
+        seqs += 1
+        if t_total >= budget_s:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = [f"{i.get('internal_api')}:{i.get('num_threads')}" for i in threadpool_info()]
+    except Exception:  # pragma: no cover - informational only
+        blas = []
+    import torch
+
+    cores = max([torch.get_num_threads()] + [int(b.split(":")[1]) for b in blas if b.split(":")[1].isdigit()])
+    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"first {seqs} of {sp.num_seqs} sequences of the same workload "
+                      f"({done_bytes / 1e6:.1f} MB of K/V, {t_total:.1f} s), fp64 numpy, "
+                      f"upcast inside the timer; thread pools: torch {torch.get_num_threads()}, "
+                      f"{', '.join(blas) or 'blas n/a'}; host cores available "
+                      f"{len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="gqa_bf16")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        sys.exit("bench.py measures one GPU only: this build has no multi-GPU path "
+                 "(decode attention shards by KV head or sequence with no exchange; see the "
+                 "design notes). Run with --gpus 1.")
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_376_amd import binding, workloads
+    from paged_kv_cache_376_amd.cache import build_cache
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a HIP device")
+    binding.lib()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    log(f"generating workload {args.config} seed {args.seed}")
+    w = workloads.make_workload(args.config, args.seed)
+    sp = w.spec
+    t0 = time.perf_counter()
+    cache = build_cache(w, dev)
+    torch.cuda.synchronize()
+    log(f"pool built in {time.perf_counter() - t0:.1f} s ({w.num_blocks} blocks)")
+
+    seqs = list(range(sp.num_seqs))
+    # Host side of the step, done once: every sequence takes the slot of its next token.
+    slots = np.zeros(sp.num_seqs, dtype=np.int64)
+    for i, s in enumerate(seqs):
+        sl, cow = cache.pool.seq_extend(s, 1)
+        cache.copy_blocks(cow)
+        slots[i] = sl[0]
+    slot_t = torch.from_numpy(slots).to(dev)
+    new_k = w.new_k.to(dev).contiguous()
+    new_v = w.new_v.to(dev).contiguous()
+    bt, ctx, maxc = cache.tables(seqs)
+    q = w.q.to(dev).contiguous()
+    out = torch.empty_like(q)
+    part = binding.paged_attn_partition_size(sp.num_seqs, sp.num_q_heads, sp.num_kv_heads,
+                                             sp.head_dim, maxc, args.partition)
+    ws_bytes = binding.paged_attn_workspace_bytes(sp.num_seqs, sp.num_q_heads, sp.num_kv_heads,
+                                                  sp.head_dim, maxc, args.partition)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        binding.kv_cache_append(new_k, new_v, cache.k_cache, cache.v_cache, slot_t, stream=stream)
+        binding.paged_attn_decode(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale,
+                                  workspace=ws, partition_size=args.partition, stream=stream)
+
+    log(f"warmup {args.warmup} steps (partition {part} tokens, workspace {ws_bytes} B)")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        binding.kv_cache_append(new_k, new_v, cache.k_cache, cache.v_cache, slot_t, stream=stream)
+        ev[i][1].record(stream)
+        binding.paged_attn_decode(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale,
+                                  workspace=ws, partition_size=args.partition, stream=stream)
+        ev[i][2].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    t_app = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
+    t_dec = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+    ms_step = total_ms / K
+    log(f"step {ms_step * 1e3:.1f} us: append {t_app.mean() * 1e3:.1f} us, decode "
+        f"median {np.median(t_dec) * 1e3:.1f} us (p10 {np.percentile(t_dec, 10) * 1e3:.1f}, "
+        f"p90 {np.percentile(t_dec, 90) * 1e3:.1f})")
+
+    def parts_of(L, pt):
+        nblk = -(-L // 16)
+        return max(1, -(-nblk // (pt // 16)))
+
+    kv_bytes, dec_bytes = algorithmic_bytes(w, part, parts_of)
+    dec_s = float(t_dec.mean()) / 1e3
+    gbs = kv_bytes / (ms_step / 1e3) / 1e9
+    achieved = dec_bytes / dec_s / 1e9
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copy done")
+
+    result = {
+        "metric": "paged decode attention KV GB/s and % HBM peak; tokens/s at 70B-GQA shape",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"float32": "f32", "float16": "f16", "bfloat16": "bf16"}[sp.dtype],
+        "data": "synthetic (seeded N(0,1) K/V/q, shuffled physical blocks)",
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s_per_layer": round(sp.num_seqs / (ms_step / 1e3), 1),
+        "decode_tokens_per_s_70b_shape_attention_only": round(sp.num_seqs / (LAYERS_70B * ms_step / 1e3), 1),
+        "append_us": round(float(t_app.mean()) * 1e3, 2),
+        "decode_us_median": round(float(np.median(t_dec)) * 1e3, 2),
+        "config": {
+            "workload": f"{sp.name}: paged decode, B={sp.num_seqs}, Hq={sp.num_q_heads}, "
+                        f"Hkv={sp.num_kv_heads}, D={sp.head_dim}, block 16, {sp.dtype}, "
+                        f"lengths {sp.lengths}, seed {args.seed}, +1 appended token per sequence",
+            "num_seqs": sp.num_seqs,
+            "kv_tokens": int(w.context_lens.sum()) + sp.num_seqs,
+            "kv_bytes_per_step": kv_bytes,
+            "partition_tokens": part,
+            "pool_blocks": w.num_blocks,
+        },
+        "roofline": {
+            "kernel": "pkv_paged_attn_decode (phase-1 decode kernel + split reduce)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": dec_bytes,
+            "avg_launch_us": round(dec_s * 1e6, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,240 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv: paged KV-cache decode attention for AMD MI355X (gfx950).
+ *
+ * The method follows three web pages on vLLM's PagedAttention, cited by title and section:
+ *   [111cn]  "大模型推理引擎高频优化：连续批处理、PagedAttention 与 KV Cache 实战拆解"
+ *   [gtnt]   "vLLM推理加速框架：PagedAttention与连续批处理技术解析"
+ *   [yunthe] "大模型推理显存优化实战：PagedAttention机制原理与vLLM连续批处理配置"
+ *
+ * Terms.  The KV cache is cut into fixed blocks of block_size tokens (16 by default,
+ * [111cn] §3.2, [yunthe] section "PagedAttention分页注意力机制原理").  Physical blocks sit
+ * anywhere in a preallocated pool; each sequence's block table lists its physical block
+ * ids in logical order ([111cn] §3.2).  A block's data has shape (block_size, heads,
+ * head_dim) ([gtnt] §2.1), and there is one pool for K and one for V, so each pool is
+ *
+ *     cache[num_blocks][block_size][num_kv_heads][head_dim]     (row-major, contiguous)
+ *
+ * and token t of a sequence with table bt lives at block bt[t / block_size], offset
+ * t % block_size.  A "slot" is physical_block * block_size + offset.
+ *
+ * Conventions for every call:
+ *   - Return codes only; nothing throws across the ABI.  On failure pkv_last_error()
+ *     (thread-local) holds a message.  A call that fails validation launches nothing and
+ *     changes no state.
+ *   - Device calls take caller-owned device pointers (any HIP device allocation, e.g.
+ *     PyTorch tensors) that must be 16-byte aligned, and a stream (a hipStream_t passed
+ *     as void*; NULL is the default stream).  They enqueue and return; errors inside the
+ *     kernels are not reported (see each call's device-side contract).
+ *   - The library never allocates device memory.
+ *   - Host pool calls are not thread-safe: one owner per pool.
+ *   - Supported by the kernels: dtype f32, f16, bf16; head_dim 64 or 128; block_size 16.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define PKV_API __attribute__((visibility("default")))
+#else
+#define PKV_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, bad size, bad shape      */
+  PKV_ERR_UNSUPPORTED = 2,        /* valid request the kernels do not implement         */
+  PKV_ERR_OUT_OF_BLOCKS = 3,      /* pool cannot cover the request; pool unchanged       */
+  PKV_ERR_NOT_FOUND = 4,          /* unknown sequence id                                 */
+  PKV_ERR_WORKSPACE_TOO_SMALL = 5,
+  PKV_ERR_HIP = 6,                /* the HIP runtime refused a launch                    */
+  PKV_ERR_ALREADY_EXISTS = 7      /* sequence id already in use                          */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+/* Shape of one of the two pools (K and V share it). */
+typedef struct {
+  int32_t num_blocks;    /* physical blocks in the pool (> 0)                    */
+  int32_t block_size;    /* tokens per block; the kernels implement 16            */
+  int32_t num_kv_heads;  /* KV heads per token (> 0)                              */
+  int32_t head_dim;      /* 64 or 128                                             */
+  int32_t dtype;         /* pkv_dtype                                             */
+} pkv_cache_desc;
+
+/* ------------------------------------------------------------------------------------ */
+/* Library                                                                               */
+/* ------------------------------------------------------------------------------------ */
+
+/* Message of the last failing call on this thread ("" if none).  Owned by the library,
+ * valid until the next call on this thread. */
+PKV_API const char* pkv_last_error(void);
+
+/* Static name of a status code. */
+PKV_API const char* pkv_status_string(int32_t status);
+
+/* Library version string, static. */
+PKV_API const char* pkv_version(void);
+
+/* ------------------------------------------------------------------------------------ */
+/* Device: KV append (the reshape-and-cache scatter)                                     */
+/* ------------------------------------------------------------------------------------ */
+
+/* Writes each new token's K and V row into its pool slot.
+ *
+ * Defined by the append step of [111cn] §3.3 (the new token goes to the end of the last
+ * block, or into a freshly taken block when the last one is full -- the host pool below
+ * decides which, and hands the result over as slots) and the block layout of [gtnt] §2.1.
+ *
+ *   key, value      device, [num_tokens][num_kv_heads][head_dim] of cache->dtype, read only
+ *   k_cache,v_cache device pools laid out as described at the top, written in place
+ *   cache           host descriptor of both pools
+ *   slot_mapping    device int64 [num_tokens]; row i goes to block slot/bs, offset slot%bs
+ *   num_tokens      >= 0 (0 is a no-op)
+ *
+ * For each i with 0 <= slot_mapping[i] < num_blocks*block_size the row is copied bit for
+ * bit; other slots (negative = padding, or out of range) are skipped without any memory
+ * access.  Two tokens with the same slot race (undefined which row wins).
+ * Errors: INVALID_ARGUMENT (null or misaligned pointer, num_tokens < 0, bad descriptor),
+ * UNSUPPORTED (dtype/head_dim/block_size outside the set above), HIP (launch failed). */
+PKV_API pkv_status pkv_kv_cache_append(const void* key, const void* value,
+                               void* k_cache, void* v_cache, const pkv_cache_desc* cache,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               void* stream);
+
+/* ------------------------------------------------------------------------------------ */
+/* Device: paged decode attention                                                        */
+/* ------------------------------------------------------------------------------------ */
+
+/* Bytes of fp32 workspace pkv_paged_attn_decode needs for these arguments (0 when the
+ * chosen partitioning does not split any sequence).  partition_size as for the decode
+ * call. Returns 0 for arguments the decode call would reject. */
+PKV_API size_t pkv_paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t max_context_len, int32_t partition_size);
+
+/* The partition size (tokens) pkv_paged_attn_decode will use for these arguments:
+ * the resolved value of partition_size 0 (auto) or -1 (never split: max_context_len
+ * rounded up to the block size), or partition_size itself.  0 on invalid arguments. */
+PKV_API int32_t pkv_paged_attn_partition_size(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t max_context_len, int32_t partition_size);
+
+/* Single-query attention of every sequence over its paged context.
+ *
+ * The kernel finds each token's physical block through the block table and attends over
+ * the non-contiguous blocks ([yunthe] section "PagedAttention分页注意力机制原理"); the
+ * result is scaled dot-product attention over the sequence's tokens in logical order:
+ *
+ *   out[s,h,:] = sum_t w_t V_s[t, h/G, :] / sum_t w_t,
+ *   w_t = exp(scale * <q[s,h,:], K_s[t, h/G, :]> - max),  t = 0 .. context_lens[s]-1,
+ *
+ * with G = num_q_heads / num_kv_heads (query head h reads KV head h / G).  The argument
+ * list extends the one of the CUDA kernel shown in [gtnt] §6.2 (out, q, k, v, block
+ * tables; out shares q's element type) with context lengths, scale, workspace and stream.
+ *
+ *   out            device [num_seqs][num_q_heads][head_dim], cache->dtype, written
+ *   q              device [num_seqs][num_q_heads][head_dim], cache->dtype
+ *   k_cache,v_cache device pools (read only)
+ *   block_tables   device int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                  ceil(context_len/bs) are never read (any value, e.g. -1)
+ *   context_lens   device int32 [num_seqs]
+ *   max_context_len host int, >= every context_lens[s], <= max_blocks_per_seq*block_size
+ *   scale          logit scale (usually 1/sqrt(head_dim))
+ *   workspace      device fp32 scratch of >= pkv_paged_attn_workspace_bytes(...) bytes
+ *                  (may be NULL when that is 0); contents on return unspecified
+ *   partition_size 0 = auto; -1 = never split; else tokens per partition, a positive
+ *                  multiple of block_size.  Sequences longer than one partition are
+ *                  processed as independent partitions and merged exactly (log-sum-exp
+ *                  combine in a fixed order), so the result is deterministic.
+ *
+ * A sequence with context length 0 yields zeros.  Results are bitwise reproducible run to
+ * run for identical inputs and arguments.
+ * Device-side contract (not checked on the host): context_lens[s] in [0, max_context_len]
+ * and table entries in [0, num_blocks).  To never touch memory outside the buffers, the
+ * kernels clamp context lengths to max_context_len and skip blocks whose id is out of
+ * range; the output is then unspecified, but nothing outside the buffers is read.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (dtype/head_dim/block_size/group size outside the
+ * implemented set: f32 supports G <= 2, f16/bf16 support G <= 16), WORKSPACE_TOO_SMALL,
+ * HIP. */
+PKV_API pkv_status pkv_paged_attn_decode(void* out, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const pkv_cache_desc* cache,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t max_context_len,
+                                 int32_t num_seqs, int32_t num_q_heads, float scale,
+                                 void* workspace, size_t workspace_bytes,
+                                 int32_t partition_size, void* stream);
+
+/* ------------------------------------------------------------------------------------ */
+/* Host: block pool and block tables                                                     */
+/* ------------------------------------------------------------------------------------ */
+
+/* The pool of [111cn] §3.2-§3.3 / [yunthe] "PagedAttention分页注意力机制原理": a free list
+ * of physical block ids, a reference count per block ([gtnt] §2.1) and one block table per
+ * sequence.  Pure host code.  Every operation is all-or-nothing: when the free list
+ * cannot cover it (the admission check of the scheduler in [111cn] §2.2), it returns
+ * PKV_ERR_OUT_OF_BLOCKS and nothing changes. */
+typedef struct pkv_block_pool pkv_block_pool;
+
+/* free_order: NULL for 0..num_blocks-1, else a permutation of 0..num_blocks-1; blocks are
+ * popped from the END of this list ([111cn] §3.3).  *out receives the new pool. */
+PKV_API pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size,
+                           const int32_t* free_order, pkv_block_pool** out);
+PKV_API void pkv_pool_destroy(pkv_block_pool* pool);
+
+PKV_API int32_t pkv_pool_num_blocks(const pkv_block_pool* pool);
+PKV_API int32_t pkv_pool_block_size(const pkv_block_pool* pool);
+PKV_API int32_t pkv_pool_num_free(const pkv_block_pool* pool);
+/* Reference count of a block, -1 if block_id is out of range. */
+PKV_API int32_t pkv_pool_ref_count(const pkv_block_pool* pool, int32_t block_id);
+/* Copies min(capacity, num_free) free-list entries (bottom first; the next pop takes the
+ * last one) into out; returns num_free. */
+PKV_API int32_t pkv_pool_free_list(const pkv_block_pool* pool, int32_t* out, int32_t capacity);
+/* Number of live sequences. */
+PKV_API int32_t pkv_pool_num_seqs(const pkv_block_pool* pool);
+
+/* New sequence holding num_tokens (>= 0) tokens: ceil(num_tokens/bs) blocks popped from
+ * the end of the free list, in logical order ([111cn] §3.3 allocate).  blocks_out
+ * (nullable) receives them.  ALREADY_EXISTS, OUT_OF_BLOCKS, INVALID_ARGUMENT. */
+PKV_API pkv_status pkv_seq_allocate(pkv_block_pool* pool, int64_t seq, int32_t num_tokens,
+                            int32_t* blocks_out);
+
+/* Appends n (>= 0) tokens ([111cn] §3.3 append_token, repeated): a token whose sequence
+ * holds a multiple of bs tokens (its last block is full, or it has none) takes a fresh
+ * block; otherwise it goes to the end of the last block.  If that last block is shared
+ * (ref > 1) and not full it is first replaced by a fresh private block (copy-on-write,
+ * [gtnt] §2.2): *num_cow_out = 1 and cow_out = {src, dst}; the caller must copy the
+ * block's bytes src -> dst in both pools before writing the new rows.  slots_out
+ * (nullable, n entries) receives each new token's slot.  NOT_FOUND, OUT_OF_BLOCKS. */
+PKV_API pkv_status pkv_seq_extend(pkv_block_pool* pool, int64_t seq, int32_t n, int64_t* slots_out,
+                          int32_t* cow_out, int32_t* num_cow_out);
+
+/* child shares every block of parent (each ref + 1) and its token count ([gtnt] §2.1-2.2,
+ * [yunthe] prefix sharing).  NOT_FOUND, ALREADY_EXISTS. */
+PKV_API pkv_status pkv_seq_fork(pkv_block_pool* pool, int64_t parent, int64_t child);
+
+/* Drops the sequence: in table order each block's ref - 1, pushed onto the end of the free
+ * list when it reaches 0 (blocks return to the pool when a request ends, [yunthe]). */
+PKV_API pkv_status pkv_seq_free(pkv_block_pool* pool, int64_t seq);
+
+/* Token count of seq, or -1 if unknown. */
+PKV_API int64_t pkv_seq_context_len(const pkv_block_pool* pool, int64_t seq);
+
+/* Block tables of seqs[0..n) as rows of tables_out[n][max_blocks_per_seq] (padded with
+ * -1) and their context lengths in context_lens_out[n] (both host, nullable each).
+ * NOT_FOUND, INVALID_ARGUMENT (a table longer than max_blocks_per_seq). */
+PKV_API pkv_status pkv_pool_block_tables(const pkv_block_pool* pool, const int64_t* seqs, int32_t n,
+                                 int32_t max_blocks_per_seq, int32_t* tables_out,
+                                 int32_t* context_lens_out);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif /* PAGEDKV_H */

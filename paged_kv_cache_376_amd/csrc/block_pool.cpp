@@ -1,0 +1,228 @@
+// Host block pool and block tables (pure C++, no HIP dependency).
+//
+// The paging scheme of the 111cn.net page "大模型推理引擎高频优化：连续批处理、PagedAttention
+// 与 KV Cache 实战拆解" §3.2-§3.3: a pool of equal physical blocks, a free list that
+// allocation pops from the end, one block table per sequence, and a fresh block only when
+// the last one is full.  Reference counts per block from the gtnt.cn page "vLLM推理加速框架：
+// PagedAttention与连续批处理技术解析" §2.1, copy-on-write of shared blocks from its §2.2, and
+// blocks returned to the pool when a request ends from the yunthe.com page "大模型推理显存
+// 优化实战：PagedAttention机制原理与vLLM连续批处理配置", section
+// "PagedAttention分页注意力机制原理".
+//
+// Every mutating call first computes how many blocks it needs and fails with
+// PKV_ERR_OUT_OF_BLOCKS before touching anything if the free list is too short.
+#include <cstring>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pkv_internal.h"
+
+struct pkv_block_pool {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> free_list;  // next allocation pops back()
+  std::vector<int32_t> ref;        // per physical block
+  struct Seq {
+    std::vector<int32_t> table;    // logical -> physical
+    int64_t num_tokens = 0;
+  };
+  std::unordered_map<int64_t, Seq> seqs;
+};
+
+namespace {
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Blocks that appending n tokens to `s` takes from the free list (incl. a CoW copy).
+int64_t blocks_needed(const pkv_block_pool* p, const pkv_block_pool::Seq& s, int64_t n) {
+  const int64_t bs = p->block_size;
+  int64_t need = ceil_div(s.num_tokens + n, bs) - ceil_div(s.num_tokens, bs);
+  if (n > 0 && s.num_tokens % bs != 0 && p->ref[s.table.back()] > 1) need += 1;
+  return need;
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size,
+                                      const int32_t* free_order, pkv_block_pool** out) {
+  pkv::clear_error();
+  if (!out) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  if (num_blocks <= 0) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "num_blocks=%d", num_blocks);
+  if (block_size <= 0) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "block_size=%d", block_size);
+  pkv_block_pool* p = new (std::nothrow) pkv_block_pool();
+  if (!p) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "host allocation failed");
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->ref.assign(num_blocks, 0);
+  p->free_list.resize(num_blocks);
+  if (free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete p;
+        return pkv::fail(PKV_ERR_INVALID_ARGUMENT,
+                         "free_order is not a permutation of 0..%d (entry %d = %d)",
+                         num_blocks - 1, i, b);
+      }
+      seen[b] = 1;
+      p->free_list[i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) p->free_list[i] = i;
+  }
+  *out = p;
+  return PKV_OK;
+}
+
+extern "C" void pkv_pool_destroy(pkv_block_pool* pool) { delete pool; }
+
+extern "C" int32_t pkv_pool_num_blocks(const pkv_block_pool* p) { return p ? p->num_blocks : -1; }
+extern "C" int32_t pkv_pool_block_size(const pkv_block_pool* p) { return p ? p->block_size : -1; }
+extern "C" int32_t pkv_pool_num_free(const pkv_block_pool* p) {
+  return p ? static_cast<int32_t>(p->free_list.size()) : -1;
+}
+extern "C" int32_t pkv_pool_num_seqs(const pkv_block_pool* p) {
+  return p ? static_cast<int32_t>(p->seqs.size()) : -1;
+}
+
+extern "C" int32_t pkv_pool_ref_count(const pkv_block_pool* p, int32_t block_id) {
+  if (!p || block_id < 0 || block_id >= p->num_blocks) return -1;
+  return p->ref[block_id];
+}
+
+extern "C" int32_t pkv_pool_free_list(const pkv_block_pool* p, int32_t* out, int32_t capacity) {
+  if (!p) return -1;
+  const int32_t n = static_cast<int32_t>(p->free_list.size());
+  if (out && capacity > 0) {
+    const int32_t m = capacity < n ? capacity : n;
+    std::memcpy(out, p->free_list.data(), sizeof(int32_t) * m);
+  }
+  return n;
+}
+
+extern "C" pkv_status pkv_seq_allocate(pkv_block_pool* p, int64_t seq, int32_t num_tokens,
+                                       int32_t* blocks_out) {
+  pkv::clear_error();
+  if (!p) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "pool is NULL");
+  if (num_tokens < 0) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "num_tokens=%d", num_tokens);
+  if (p->seqs.count(seq)) return pkv::fail(PKV_ERR_ALREADY_EXISTS, "sequence %lld exists", (long long)seq);
+  const int64_t need = ceil_div(num_tokens, p->block_size);
+  if (need > static_cast<int64_t>(p->free_list.size()))
+    return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "allocate needs %lld blocks, %zu free",
+                     (long long)need, p->free_list.size());
+  pkv_block_pool::Seq s;
+  s.table.reserve(need);
+  for (int64_t i = 0; i < need; ++i) {
+    const int32_t b = p->free_list.back();
+    p->free_list.pop_back();
+    p->ref[b] = 1;
+    s.table.push_back(b);
+    if (blocks_out) blocks_out[i] = b;
+  }
+  s.num_tokens = num_tokens;
+  p->seqs.emplace(seq, std::move(s));
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_extend(pkv_block_pool* p, int64_t seq, int32_t n, int64_t* slots_out,
+                                     int32_t* cow_out, int32_t* num_cow_out) {
+  pkv::clear_error();
+  if (num_cow_out) *num_cow_out = 0;
+  if (!p) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "pool is NULL");
+  if (n < 0) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "n=%d", n);
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return pkv::fail(PKV_ERR_NOT_FOUND, "sequence %lld", (long long)seq);
+  pkv_block_pool::Seq& s = it->second;
+  const int64_t need = blocks_needed(p, s, n);
+  if (need > static_cast<int64_t>(p->free_list.size()))
+    return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "extend by %d needs %lld blocks, %zu free", n,
+                     (long long)need, p->free_list.size());
+  const int64_t bs = p->block_size;
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t offset = s.num_tokens % bs;
+    if (offset == 0) {  // last block full, or no block yet: take a fresh one
+      const int32_t b = p->free_list.back();
+      p->free_list.pop_back();
+      p->ref[b] = 1;
+      s.table.push_back(b);
+    } else if (p->ref[s.table.back()] > 1) {  // shared, partly filled: copy on write
+      const int32_t src = s.table.back();
+      const int32_t dst = p->free_list.back();
+      p->free_list.pop_back();
+      p->ref[src] -= 1;
+      p->ref[dst] = 1;
+      s.table.back() = dst;
+      if (cow_out) {
+        cow_out[0] = src;
+        cow_out[1] = dst;
+      }
+      if (num_cow_out) *num_cow_out = 1;  // only the first appended token can trigger it
+    }
+    if (slots_out) slots_out[i] = static_cast<int64_t>(s.table.back()) * bs + offset;
+    s.num_tokens += 1;
+  }
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_fork(pkv_block_pool* p, int64_t parent, int64_t child) {
+  pkv::clear_error();
+  if (!p) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "pool is NULL");
+  auto it = p->seqs.find(parent);
+  if (it == p->seqs.end()) return pkv::fail(PKV_ERR_NOT_FOUND, "sequence %lld", (long long)parent);
+  if (p->seqs.count(child)) return pkv::fail(PKV_ERR_ALREADY_EXISTS, "sequence %lld exists", (long long)child);
+  pkv_block_pool::Seq c = it->second;  // copy: table and token count
+  for (int32_t b : c.table) p->ref[b] += 1;
+  p->seqs.emplace(child, std::move(c));
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_free(pkv_block_pool* p, int64_t seq) {
+  pkv::clear_error();
+  if (!p) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "pool is NULL");
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return pkv::fail(PKV_ERR_NOT_FOUND, "sequence %lld", (long long)seq);
+  for (int32_t b : it->second.table) {
+    if (--p->ref[b] == 0) p->free_list.push_back(b);
+  }
+  p->seqs.erase(it);
+  return PKV_OK;
+}
+
+extern "C" int64_t pkv_seq_context_len(const pkv_block_pool* p, int64_t seq) {
+  if (!p) return -1;
+  auto it = p->seqs.find(seq);
+  return it == p->seqs.end() ? -1 : it->second.num_tokens;
+}
+
+extern "C" pkv_status pkv_pool_block_tables(const pkv_block_pool* p, const int64_t* seqs, int32_t n,
+                                            int32_t max_blocks_per_seq, int32_t* tables_out,
+                                            int32_t* context_lens_out) {
+  pkv::clear_error();
+  if (!p) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "pool is NULL");
+  if (n < 0 || (n > 0 && !seqs)) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "n=%d seqs=%p", n, (const void*)seqs);
+  if (max_blocks_per_seq < 0) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "max_blocks_per_seq=%d", max_blocks_per_seq);
+  // validate everything before writing anything
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = p->seqs.find(seqs[i]);
+    if (it == p->seqs.end()) return pkv::fail(PKV_ERR_NOT_FOUND, "sequence %lld", (long long)seqs[i]);
+    if (static_cast<int64_t>(it->second.table.size()) > max_blocks_per_seq)
+      return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "sequence %lld has %zu blocks > max_blocks_per_seq %d",
+                       (long long)seqs[i], it->second.table.size(), max_blocks_per_seq);
+    if (it->second.num_tokens > INT32_MAX)
+      return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "context length overflows int32");
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const auto& s = p->seqs.find(seqs[i])->second;
+    if (tables_out) {
+      int32_t* row = tables_out + static_cast<int64_t>(i) * max_blocks_per_seq;
+      const int32_t len = static_cast<int32_t>(s.table.size());
+      for (int32_t j = 0; j < len; ++j) row[j] = s.table[j];
+      for (int32_t j = len; j < max_blocks_per_seq; ++j) row[j] = -1;
+    }
+    if (context_lens_out) context_lens_out[i] = static_cast<int32_t>(s.num_tokens);
+  }
+  return PKV_OK;
+}

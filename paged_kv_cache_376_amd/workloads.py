@@ -143,8 +143,12 @@ class Workload:
         else:
             need = sum(_blocks(int(L) + 1, bs) for L in self.context_lens)
             if self.groups is not None:
-                shared = _blocks(spec.prefix_len, bs)
+                # whole prefix blocks are shared; a partly filled last prefix block is
+                # copied by every member on its first append (copy-on-write)
+                shared = spec.prefix_len // bs
                 need -= shared * (B - len(self.groups))
+                if spec.prefix_len % bs:
+                    need += len(self.groups)  # the original partial block, until freed
             nb = int(math.ceil(1.1 * need))
         self.num_blocks = nb
         self.free_order = np.random.default_rng(streams[_S_FREE]).permutation(nb).astype(np.int32)

@@ -1,0 +1,201 @@
+"""CPU tests of the C ABI: the library loads, exports what include/pagedkv.h declares, the
+host pool agrees with the oracle's block manager, and the device entry points reject bad
+arguments before touching the GPU (no compute call is made here)."""
+
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from oracle.block_manager import BlockManager, OutOfBlocks as OracleOOB
+from paged_kv_cache_376_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+
+def _declared():
+    text = open(HEADER, encoding="utf-8").read()
+    return sorted(set(re.findall(r"PKV_API[^;(]*?\b(pkv_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = _declared()
+    assert len(names) >= 20
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.SIGNATURES), "binding and header disagree"
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in B.version()
+    lib = B.lib()
+    assert lib.pkv_status_string(3) == b"PKV_ERR_OUT_OF_BLOCKS"
+    assert lib.pkv_status_string(99) == b"PKV_ERR_UNKNOWN"
+
+
+# ------------------------------------------------------------------ host pool vs oracle
+def _both_run(pool, bm, op):
+    """Apply one op to the C++ pool and to the oracle; compare results and errors."""
+    kind, a, b, n = op
+    res_c = res_o = None
+    err_c = err_o = None
+    try:
+        if kind == "allocate":
+            res_c = pool.seq_allocate(a, n)
+        elif kind == "extend":
+            s, c = pool.seq_extend(a, n)
+            res_c = (s.tolist(), c)
+        elif kind == "fork":
+            pool.seq_fork(a, b)
+        else:
+            pool.seq_free(a)
+    except B.PkvError as e:
+        err_c = e.status_name
+    try:
+        if kind == "allocate":
+            res_o = bm.allocate(a, n)
+        elif kind == "extend":
+            s, c = bm.extend(a, n)
+            res_o = (s, [tuple(x) for x in c])
+        elif kind == "fork":
+            bm.fork(a, b)
+        else:
+            bm.free(a)
+    except OracleOOB:
+        err_o = "PKV_ERR_OUT_OF_BLOCKS"
+    except KeyError as e:
+        err_o = "PKV_ERR_ALREADY_EXISTS" if "exists" in str(e) else "PKV_ERR_NOT_FOUND"
+    assert err_c == err_o, (op, err_c, err_o)
+    assert res_c == res_o, (op, res_c, res_o)
+
+
+def _same_state(pool, bm):
+    assert pool.free_list() == bm.free_blocks
+    assert [pool.ref_count(i) for i in range(bm.num_blocks)] == bm.ref_count
+    seqs = sorted(bm.block_tables)
+    assert pool.num_seqs() == len(seqs)
+    if seqs:
+        maxb = max(1, max(len(t) for t in bm.block_tables.values()))
+        tables, lens = pool.block_tables(seqs, maxb)
+        et, el = bm.tables(seqs, maxb)
+        assert tables.tolist() == et and lens.tolist() == el
+
+
+def test_pool_replays_hand_worked_history():
+    with open(os.path.join(ROOT, "tests", "golden", "block_manager_worked.json"), encoding="utf-8") as f:
+        fx = json.load(f)
+    pool = B.BlockPool(fx["num_blocks"], fx["block_size"], fx["free_order"])
+    bm = BlockManager(fx["num_blocks"], fx["block_size"], fx["free_order"])
+    for op in fx["ops"]:
+        tup = (op["op"], op.get("seq", op.get("parent")), op.get("child", 0), op.get("n", 0))
+        _both_run(pool, bm, tup)
+        assert pool.free_list() == op["free_after"]
+        _same_state(pool, bm)
+    assert pool.block_tables([3], 4)[0].tolist() == [fx["tables_after"]["final"]["3"]]
+
+
+_ops = st.lists(st.tuples(st.sampled_from(["allocate", "extend", "fork", "free"]),
+                          st.integers(0, 5), st.integers(0, 5), st.integers(0, 40)), max_size=60)
+
+
+@settings(max_examples=300, deadline=None)
+@given(ops=_ops, nb=st.integers(1, 24), bs=st.sampled_from([1, 2, 4, 16]), seed=st.integers(0, 1000))
+def test_pool_matches_oracle_on_random_histories(ops, nb, bs, seed):
+    order = np.random.default_rng(seed).permutation(nb).astype(np.int32)
+    pool = B.BlockPool(nb, bs, order)
+    bm = BlockManager(nb, bs, order.tolist())
+    for op in ops:
+        _both_run(pool, bm, op)
+        _same_state(pool, bm)
+
+
+def test_pool_rejects_bad_free_order_and_sizes():
+    with pytest.raises(B.PkvError) as e:
+        B.BlockPool(4, 16, [0, 1, 1, 3])
+    assert e.value.status_name == "PKV_ERR_INVALID_ARGUMENT"
+    with pytest.raises(B.PkvError):
+        B.BlockPool(0, 16)
+    with pytest.raises(B.PkvError):
+        B.BlockPool(4, 0)
+    p = B.BlockPool(4, 16)
+    with pytest.raises(B.PkvError):
+        p.seq_allocate(1, -1)
+    p.seq_allocate(1, 40)
+    with pytest.raises(B.PkvError) as e:
+        p.block_tables([1], 2)  # table of 3 blocks does not fit 2 columns
+    assert e.value.status_name == "PKV_ERR_INVALID_ARGUMENT"
+    assert p.seq_context_len(1) == 40 and p.seq_context_len(2) == -1
+    assert p.ref_count(-1) == -1 and p.ref_count(4) == -1
+
+
+# ------------------------------------------------------------------ device-call validation
+def _desc(nb=8, bs=16, hkv=2, d=128, dt=2):
+    return B.CacheDesc(nb, bs, hkv, d, dt)
+
+
+def _decode(desc, **kw):
+    a = dict(out=16, q=16, k=16, v=16, bt=16, maxb=4, ctx=16, maxc=64, B=2, hq=4, scale=0.1,
+             ws=None, wsb=0, part=-1)
+    a.update(kw)
+    lib = B.lib()
+    return lib.pkv_paged_attn_decode(a["out"], a["q"], a["k"], a["v"], ctypes.byref(desc), a["bt"],
+                                     a["maxb"], a["ctx"], a["maxc"], a["B"], a["hq"], a["scale"],
+                                     a["ws"], a["wsb"], a["part"], None)
+
+
+@pytest.mark.parametrize("kw,desc_kw,expect", [
+    ({"out": None}, {}, 1),                      # null pointer
+    ({"q": 24}, {}, 1),                          # misaligned pointer
+    ({}, {"d": 96}, 2),                          # head_dim not implemented
+    ({}, {"bs": 8}, 2),                          # block size not implemented
+    ({}, {"dt": 7}, 2),                          # unknown dtype
+    ({"hq": 5}, {}, 1),                          # Hq not a multiple of Hkv
+    ({"hq": 40}, {}, 2),                         # G = 20 > 16
+    ({"hq": 6}, {"dt": 0}, 2),                   # fp32 with G = 3
+    ({"maxc": 65}, {}, 1),                       # max_context_len > maxb * bs
+    ({"part": 24}, {}, 1),                       # partition not a multiple of 16
+    ({"part": 16, "maxc": 64}, {}, 5),           # split needs a workspace
+    ({"scale": float("nan")}, {}, 1),
+    ({"B": -1}, {}, 1),
+    ({}, {"nb": 0}, 1),
+])
+def test_decode_rejects_before_launch(kw, desc_kw, expect):
+    assert _decode(_desc(**desc_kw), **kw) == expect
+    assert B.lib().pkv_last_error() != b""
+
+
+def test_decode_with_no_sequences_is_a_noop():
+    assert _decode(_desc(), B=0, out=None, q=None) == 0
+
+
+def test_workspace_size_and_partition_rules():
+    ws = B.paged_attn_workspace_bytes
+    ps = B.paged_attn_partition_size
+    assert ws(256, 64, 8, 128, 8192, -1) == 0
+    assert ps(256, 64, 8, 128, 8192, -1) == 8192
+    assert ps(4, 4, 4, 64, 100, -1) == 112
+    assert ps(8, 32, 8, 128, 32768, 1024) == 1024
+    assert ps(8, 32, 8, 128, 32768, 24) == 0
+    assert ws(8, 32, 8, 128, 32768, 1024) == 8 * 32 * 32 * 130 * 4
+    auto = ps(256, 64, 8, 128, 8192, 0)
+    assert auto % 16 == 0 and auto > 0
+    P = -(-8192 // auto)
+    assert ws(256, 64, 8, 128, 8192, 0) == (0 if P == 1 else 256 * 64 * P * 130 * 4)
+    assert ws(4, 4, 4, 64, 100, 0) == 0
+
+
+def test_append_rejects_before_launch():
+    lib = B.lib()
+    d = _desc()
+    assert lib.pkv_kv_cache_append(16, 16, 16, 16, ctypes.byref(d), 16, -1, None) == 1
+    assert lib.pkv_kv_cache_append(None, 16, 16, 16, ctypes.byref(d), 16, 3, None) == 1
+    assert lib.pkv_kv_cache_append(16, 16, 16, 8, ctypes.byref(d), 16, 3, None) == 1
+    assert lib.pkv_kv_cache_append(16, 16, 16, 16, ctypes.byref(_desc(d=80)), 16, 3, None) == 2
+    assert lib.pkv_kv_cache_append(16, 16, 16, 16, None, 16, 3, None) == 1
+    assert lib.pkv_kv_cache_append(16, 16, 16, 16, ctypes.byref(d), 16, 0, None) == 0

@@ -1,0 +1,163 @@
+"""GPU invariants of paged decode: properties fixed by the definition, checked bit for bit
+where rounding cannot enter, on both kernel variants (VALU: G <= 2, MFMA: G > 2)."""
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_376_amd import workloads as W
+from paged_kv_cache_376_amd.cache import PagedKVCache
+from tests.gpu_common import DEVICE, TOL, bits, decode, decode_step, max_err, oracle_out, say
+
+pytestmark = pytest.mark.gpu
+
+# (dtype, Hq, Hkv, D): VALU fp32 / fp16 / bf16, MFMA bf16 / fp16
+VARIANTS = [("float32", 4, 4, 64), ("float16", 8, 8, 128), ("bfloat16", 2, 1, 128),
+            ("bfloat16", 16, 2, 128), ("float16", 8, 2, 64)]
+
+
+def _spec(dtype, hq, hkv, d, lens):
+    return W.Spec("inv", dtype, len(lens), hq, hkv, d, "fixed", fixed_lengths=tuple(lens))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_block_relabel_is_bitwise_invariant(variant):
+    """I-1: a different assignment of physical blocks gives the identical output."""
+    say(f"[inv relabel] {variant}")
+    w = W.Workload(_spec(*variant, (300, 17, 1000)), seed=1)
+    a, *_ = decode_step(w, partition_size=64)
+    w.free_order = np.random.default_rng(99).permutation(w.num_blocks).astype(np.int32)
+    b, *_ = decode_step(w, partition_size=64)
+    assert torch.equal(bits(a), bits(b))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_context_of_one_returns_v_row(variant):
+    """I-2: with one token the output is that token's V row, bit for bit."""
+    say(f"[inv ctx1] {variant}")
+    dtype, hq, hkv, d = variant
+    w = W.Workload(_spec(*variant, (0, 0, 0)), seed=2)
+    out, *_ = decode_step(w)
+    G = hq // hkv
+    expect = w.new_v.repeat_interleave(G, dim=1)
+    assert torch.equal(bits(out), bits(expect))
+
+
+@pytest.mark.parametrize("partition", [0, 32])
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_one_hot_probe_selects_exact_row(variant, partition):
+    """I-3: a query that matches one key by a logit gap of ~360 returns exactly that key's
+    V row; swept over block and partition boundaries, this pins the gather indexing."""
+    dtype, hq, hkv, d = variant
+    say(f"[inv one-hot] {variant} partition={partition}")
+    tdt = getattr(torch, dtype)
+    L = 200
+    rng = np.random.default_rng(4)
+    order = rng.permutation(64).astype(np.int32)
+    v = torch.from_numpy(rng.standard_normal((L, hkv, d), dtype=np.float32)).to(tdt)
+    q = torch.zeros((1, hq, d), dtype=tdt)
+    q[..., 0] = 8.0
+    for t_star in (0, 15, 16, 17, 31, 32, 63, 64, 100, 199):
+        k = torch.zeros((L, hkv, d), dtype=tdt)
+        k[:, :, 0] = -256.0
+        k[t_star, :, 0] = 256.0
+        cache = PagedKVCache(64, hkv, d, tdt, DEVICE, free_order=order, fill=float("nan"))
+        cache.add_sequence(0, k, v)
+        bt, ctx, maxc = cache.tables([0])
+        out = decode(cache, q, bt, ctx, maxc, 1.0 / np.sqrt(d), partition)
+        expect = v[t_star].repeat_interleave(hq // hkv, dim=0)
+        assert torch.equal(bits(out[0]), bits(expect)), f"t*={t_star}"
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_constant_v_gives_constant(variant):
+    """I-4: weights sum to 1 -- V == 1 everywhere gives 1 (exactly, after rounding to a
+    16-bit type; within a few ulp in fp32)."""
+    dtype, hq, hkv, d = variant
+    say(f"[inv V=1] {variant}")
+    tdt = getattr(torch, dtype)
+    rng = np.random.default_rng(6)
+    cache = PagedKVCache(128, hkv, d, tdt, DEVICE, free_order=rng.permutation(128), fill=float("nan"))
+    lens = (1, 16, 17, 500, 1100)
+    for s, L in enumerate(lens):
+        k = torch.from_numpy(rng.standard_normal((L, hkv, d), dtype=np.float32)).to(tdt)
+        cache.add_sequence(s, k, torch.ones((L, hkv, d), dtype=tdt))
+    q = torch.from_numpy(rng.standard_normal((len(lens), hq, d), dtype=np.float32)).to(tdt)
+    bt, ctx, maxc = cache.tables(range(len(lens)))
+    for partition in (0, -1, 48):
+        out = decode(cache, q, bt, ctx, maxc, 1.0 / np.sqrt(d), partition)
+        if dtype == "float32":
+            assert float((out - 1).abs().max()) <= 4e-7
+        else:
+            assert torch.equal(out, torch.ones_like(out))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_shared_prefix_and_copy_give_identical_outputs(variant):
+    """I-5: sequences reading the same physical blocks (fork) or an equal private copy,
+    with the same query, produce identical outputs."""
+    dtype, hq, hkv, d = variant
+    say(f"[inv shared] {variant}")
+    tdt = getattr(torch, dtype)
+    rng = np.random.default_rng(7)
+    L = 333
+    k = torch.from_numpy(rng.standard_normal((L, hkv, d), dtype=np.float32)).to(tdt)
+    v = torch.from_numpy(rng.standard_normal((L, hkv, d), dtype=np.float32)).to(tdt)
+    cache = PagedKVCache(96, hkv, d, tdt, DEVICE, free_order=rng.permutation(96), fill=float("nan"))
+    cache.add_sequence(0, k, v)
+    for c in (1, 2, 3):
+        cache.fork(0, c)
+    cache.add_sequence(4, k, v)
+    assert cache.pool.ref_count(int(cache.pool.block_tables([0], 21)[0][0, 0])) == 4
+    q1 = torch.from_numpy(rng.standard_normal((1, hq, d), dtype=np.float32)).to(tdt)
+    q = q1.repeat(5, 1, 1)
+    bt, ctx, maxc = cache.tables(range(5))
+    for partition in (0, 64):
+        out = decode(cache, q, bt, ctx, maxc, 1.0 / np.sqrt(d), partition)
+        for s in range(1, 5):
+            assert torch.equal(bits(out[s]), bits(out[0])), s
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_bitwise_deterministic(variant):
+    """I-6: identical inputs give identical bits run to run."""
+    say(f"[inv determinism] {variant}")
+    w = W.Workload(_spec(*variant, (900, 33, 2000, 5)), seed=8)
+    out, cache, bt, ctx, maxc = decode_step(w, partition_size=64)
+    again = decode(cache, w.q, bt, ctx, maxc, w.scale, 64)
+    assert torch.equal(bits(out), bits(again))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_split_agrees_with_unsplit(variant):
+    """I-7: splitting a context into partitions changes only rounding."""
+    say(f"[inv split] {variant}")
+    w = W.Workload(_spec(*variant, (1500, 700)), seed=9)
+    whole, cache, bt, ctx, maxc = decode_step(w, partition_size=-1)
+    for part in (16, 48, 512):
+        split = decode(cache, w.q, bt, ctx, maxc, w.scale, part)
+        assert float((split.double() - whole.double()).abs().max()) <= TOL[variant[0]]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_nan_canaries_beyond_the_context_are_never_read(variant):
+    """I-8: unused slots, free blocks and table tails point at NaN data; the output stays
+    finite and matches the oracle.  A zero-length context gives zeros."""
+    dtype, hq, hkv, d = variant
+    say(f"[inv canaries] {variant}")
+    w = W.Workload(_spec(*variant, (40, 3, 250)), seed=10)
+    out, cache, bt, ctx, maxc = decode_step(w)
+    assert max_err(out, oracle_out(w)) <= TOL[dtype]
+    # table tails -> a free block full of NaN; lengths padded past the longest context
+    free_block = cache.pool.free_list()[0]
+    wide = torch.full((bt.shape[0], bt.shape[1] + 4), free_block, dtype=torch.int32, device=DEVICE)
+    wide[:, :bt.shape[1]] = torch.where(bt >= 0, bt, torch.full_like(bt, free_block))
+    for part in (0, 16, -1):
+        o2 = decode(cache, w.q, wide, ctx, maxc + 60, w.scale, part)
+        assert torch.isfinite(o2.float()).all()
+        assert max_err(o2, oracle_out(w)) <= TOL[dtype]
+    zero_ctx = ctx.clone()
+    zero_ctx[1] = 0
+    o3 = decode(cache, w.q, bt, zero_ctx, maxc, w.scale)
+    assert torch.equal(o3[1], torch.zeros_like(o3[1]))
+    assert torch.equal(bits(o3[0]), bits(out[0]))

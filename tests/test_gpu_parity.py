@@ -1,0 +1,97 @@
+"""GPU parity of the whole decode step (append + paged decode) against the fp64 oracle.
+
+Small variants of the five workloads are compared element by element; the full-size
+workloads (the shapes and launch configuration the benchmark times) on sampled sequences.
+Pools start filled with NaN, so any read of a slot the step does not own shows up.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_376_amd import workloads as W
+from tests.gpu_common import TOL, decode_step, max_err, oracle_out, say
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny_fp32": {},
+    "mha_fp16": {"num_seqs": 6, "len_lo": 100, "len_hi": 700},
+    "gqa_bf16": {"num_seqs": 12, "len_hi": 1500},
+    "long_bf16": {"num_seqs": 2, "fixed_lengths": (3000, 2047)},
+    "prefix_bf16": {"num_seqs": 16, "prefix_len": 64, "suffix_hi": 100},
+    # a prefix that ends inside a block: members copy that block on their first append
+    "prefix_bf16_cow": {"num_seqs": 16, "prefix_len": 40, "suffix_hi": 30},
+}
+
+
+def _spec(key):
+    base = "prefix_bf16" if key == "prefix_bf16_cow" else key
+    return W.SPECS[base].replace(**SMALL[key])
+
+
+@pytest.mark.parametrize("partition", [0, -1, 16, 64])
+@pytest.mark.parametrize("key", list(SMALL))
+def test_small_workload_matches_oracle(key, partition):
+    spec = _spec(key)
+    say(f"[parity small] {key} partition={partition}")
+    w = W.Workload(spec, seed=0)
+    out, *_ = decode_step(w, partition_size=partition)
+    ref = oracle_out(w)
+    err = max_err(out, ref)
+    say(f"    max abs err {err:.3e}")
+    assert torch.isfinite(out.float()).all()
+    assert err <= TOL[spec.dtype], err
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+def test_small_gqa_other_seeds(seed):
+    spec = _spec("gqa_bf16")
+    say(f"[parity small seed] gqa_bf16 seed={seed}")
+    w = W.Workload(spec, seed=seed)
+    out, *_ = decode_step(w)
+    assert max_err(out, oracle_out(w)) <= TOL[spec.dtype]
+
+
+@pytest.mark.parametrize("name", ["mha_fp16", "gqa_bf16", "long_bf16", "prefix_bf16"])
+def test_full_size_sampled(name):
+    """Full workload in the benchmark's launch configuration; sampled sequences checked."""
+    say(f"[parity full] {name}")
+    w = W.make_workload(name, 0)
+    out, *_ = decode_step(w)
+    assert torch.isfinite(out.float()).all()
+    lens = w.context_lens
+    rng = np.random.default_rng(11)
+    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
+    pick |= set(rng.choice(w.spec.num_seqs, size=min(6, w.spec.num_seqs), replace=False).tolist())
+    seqs = sorted(pick)
+    ref = oracle_out(w, seqs)
+    err = max_err(out[seqs], ref)
+    say(f"    sampled seqs {seqs}: max abs err {err:.3e}")
+    assert err <= TOL[w.spec.dtype], err
+
+
+SHAPES = [
+    # dtype, Hq, Hkv, D, context lengths (before the appended token)
+    ("float32", 2, 2, 128, (5, 15, 16, 31)),     # VALU, fp32, G=1
+    ("float32", 4, 2, 64, (0, 40, 100)),         # VALU, fp32, G=2
+    ("bfloat16", 4, 4, 128, (33, 16, 200)),      # VALU, bf16, G=1
+    ("float16", 8, 4, 64, (70, 3, 512)),         # VALU, fp16, G=2, D=64
+    ("bfloat16", 8, 2, 128, (100, 17, 600)),     # MFMA, G=4
+    ("float16", 16, 2, 128, (260, 1, 47)),       # MFMA, fp16, G=8
+    ("bfloat16", 12, 4, 64, (90, 48, 333)),      # MFMA, G=3, D=64
+    ("bfloat16", 32, 2, 128, (130, 15)),         # MFMA, G=16
+    ("float16", 10, 2, 64, (77, 513)),           # MFMA, fp16, G=5, D=64
+]
+
+
+@pytest.mark.parametrize("partition", [0, 32])
+@pytest.mark.parametrize("dtype,hq,hkv,d,lens", SHAPES)
+def test_shapes_match_oracle(dtype, hq, hkv, d, lens, partition):
+    say(f"[parity shape] {dtype} Hq={hq} Hkv={hkv} D={d} lens={lens} partition={partition}")
+    spec = W.Spec("shape", dtype, len(lens), hq, hkv, d, "fixed", fixed_lengths=tuple(lens))
+    w = W.Workload(spec, seed=5)
+    out, *_ = decode_step(w, partition_size=partition)
+    err = max_err(out, oracle_out(w))
+    say(f"    max abs err {err:.3e}")
+    assert err <= TOL[dtype], err
