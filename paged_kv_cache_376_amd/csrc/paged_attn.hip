@@ -37,6 +37,7 @@
 
 #include "dtypes.h"
 #include "pkv_internal.h"
+#include "stream_k.h"
 
 namespace pkv {
 namespace {
@@ -544,18 +545,31 @@ hipError_t launch_dtype(const Params& p, int D, int G, hipStream_t stream) {
 
 using namespace pkv;
 
+namespace {
+// The evenly split path serves partition_size 0 for grouped queries (G > 2, which the
+// kernels only implement for 16-bit types) up to kSkMaxSeqs sequences.
+bool use_stream_k(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t partition_size) {
+  return partition_size == 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 &&
+         num_q_heads / num_kv_heads > 2 && num_seqs <= sk::kSkMaxSeqs;
+}
+}  // namespace
+
 extern "C" int32_t pkv_paged_attn_partition_size(int32_t num_seqs, int32_t num_q_heads,
                                                  int32_t num_kv_heads, int32_t head_dim,
                                                  int32_t max_context_len, int32_t partition_size) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+  if (max_context_len < 0) return 0;
+  if (use_stream_k(num_seqs, num_q_heads, num_kv_heads, partition_size)) return 0;
   return resolve_partition(max_context_len, partition_size);
 }
 
 extern "C" size_t pkv_paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                                  int32_t num_kv_heads, int32_t head_dim,
                                                  int32_t max_context_len, int32_t partition_size) {
-  const int32_t part = pkv_paged_attn_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                     max_context_len, partition_size);
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  if (use_stream_k(num_seqs, num_q_heads, num_kv_heads, partition_size))
+    return num_seqs == 0 ? 0 : sk::sk_workspace_bytes(num_seqs, num_kv_heads, head_dim, max_context_len);
+  const int32_t part = resolve_partition(max_context_len, partition_size);
   if (part == 0) return 0;
   const int32_t P = parts_for(max_context_len, part);
   if (P <= 1) return 0;
@@ -593,7 +607,8 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, const void* q, const void
     return fail(PKV_ERR_INVALID_ARGUMENT, "max_context_len %d vs max_blocks_per_seq %d",
                 max_context_len, max_blocks_per_seq);
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARGUMENT, "scale is not finite");
-  const int32_t part = resolve_partition(max_context_len, partition_size);
+  const bool sk_path = use_stream_k(num_seqs, num_q_heads, cache->num_kv_heads, partition_size);
+  const int32_t part = sk_path ? kBlock : resolve_partition(max_context_len, partition_size);
   if (part == 0) return fail(PKV_ERR_INVALID_ARGUMENT, "partition_size %d", partition_size);
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !context_lens || (max_blocks_per_seq > 0 && !block_tables))
@@ -601,6 +616,37 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, const void* q, const void
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
       (reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
     return fail(PKV_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  if (sk_path) {
+    if (cache->dtype == PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "group size %d needs f16/bf16", G);
+    const size_t need = sk::sk_workspace_bytes(num_seqs, cache->num_kv_heads, D, max_context_len);
+    if (!workspace || workspace_bytes < need)
+      return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", need, workspace ? workspace_bytes : 0);
+    if (!aligned16(workspace)) return fail(PKV_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    sk::SkParams sp;
+    sp.out = out;
+    sp.q = q;
+    sp.k_cache = k_cache;
+    sp.v_cache = v_cache;
+    sp.block_tables = block_tables;
+    sp.context_lens = context_lens;
+    sp.num_seqs = num_seqs;
+    sp.num_q_heads = num_q_heads;
+    sp.num_kv_heads = cache->num_kv_heads;
+    sp.group = G;
+    sp.head_dim = D;
+    sp.max_blocks_per_seq = max_blocks_per_seq;
+    sp.max_context_len = max_context_len;
+    sp.num_blocks = cache->num_blocks;
+    sp.ranges = sk::sk_ranges(num_seqs, cache->num_kv_heads, max_context_len);
+    sp.scale_log2e = scale * kLog2e;
+    const int64_t recs = static_cast<int64_t>(sp.ranges) * sp.num_kv_heads * 2;
+    sp.ws_acc = static_cast<float*>(workspace);
+    sp.ws_ml = sp.ws_acc + recs * 16 * D;
+    sp.ws_cu = reinterpret_cast<int32_t*>(sp.ws_ml + recs * 32);
+    const hipError_t err = sk::sk_launch(sp, cache->dtype, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
+    return PKV_OK;
+  }
   const int32_t P = parts_for(max_context_len, part);
   if (num_seqs > 65535 || P > 65535)
     return fail(PKV_ERR_UNSUPPORTED, "grid too large (num_seqs %d, partitions %d)", num_seqs, P);

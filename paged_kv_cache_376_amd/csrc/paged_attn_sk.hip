@@ -1,0 +1,458 @@
+// Paged decode attention, grouped-query MFMA path with an even split of the work over the GPU.
+//
+// What is computed is the same as in paged_attn.hip: for every sequence and query head,
+// single-query scaled dot-product attention over the sequence's context, whose K/V rows sit
+// in 16-token blocks scattered through a pool and are found through the block table (the
+// yunthe.com page "大模型推理显存优化实战：PagedAttention机制原理与vLLM连续批处理配置",
+// section "PagedAttention分页注意力机制原理"; block table and 16-token blocks: the 111cn.net
+// page "大模型推理引擎高频优化：连续批处理、PagedAttention 与 KV Cache 实战拆解" §3.2; block
+// layout (block_size, heads, head_dim): the gtnt.cn page "vLLM推理加速框架：PagedAttention与
+// 连续批处理技术解析" §2.1).  This file only changes how the work is spread over the chip.
+//
+// Work split.  A "tile" is one 16-token block of one sequence for one KV head (K and V:
+// 2*16*D*e bytes).  For one KV head the tiles of all sequences form a list in sequence order
+// (block 0..nblk-1 of sequence 0, then sequence 1, ...), T tiles long.  The list is cut into
+// `ranges` equal contiguous ranges.  A work-group of 4 waves serves one range for 4
+// consecutive KV heads, one head per wave, so the waves of a work-group read neighbouring
+// 256-byte slices of the same token rows at the same time.  Every wave therefore streams
+// the same number of tiles (+-1) whatever the length mix, and keeps loading across sequence
+// boundaries.
+//   * A sequence whose tiles lie inside one range is finished by that wave (output written).
+//   * A sequence cut by range boundaries leaves one record (unnormalised acc, running max m,
+//     sum l) per wave that touched it; the merge kernel combines them in wave order.
+// Each work-group derives its range from the context lengths itself (prefix sum of block
+// counts in LDS), so no planning launch is needed.
+//
+// Per tile (one wave, 16 tokens, G <= 16 query heads padded to 16):
+//   S^T = K * Q^T            v_mfma_f32_16x16x32_{bf16,f16}, K straight from HBM as the A operand
+//   online softmax in base 2 (scale*log2(e) folded in), rescale only when some head's
+//   running max grows by more than 8 (exact: the stale max only bounds P by 2^8)
+//   O^T += V^T * P^T         v_mfma_f32_16x16x16, V^T read from an LDS copy of the V tile with
+//                            ds_read_b64_tr_b16 (one transposing read per 16-column chunk)
+// Loads use buffer resources so that a slot past the end of the range is a zero-length load
+// (no memory access) and the pipeline stays unconditional.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "dtypes.h"
+#include "pkv_internal.h"
+#include "stream_k.h"
+
+namespace pkv {
+namespace sk {
+namespace {
+
+constexpr int kBlock = 16;
+constexpr int kWaves = 4;                 // KV heads (waves) per work-group
+constexpr int kThreads = 64 * kWaves;
+constexpr float kNegBig = -1.0e30f;
+constexpr float kTau = 8.0f;              // lazy-rescale threshold (log2 units)
+constexpr int kLast = 1 << 8;             // tile flag: last block of its sequence
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // buffer descriptor dword 3 for gfx9-class parts
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+
+template <typename T> struct Mma;
+template <> struct Mma<BF16> {
+  using v8 = bf16x8;
+  __device__ static f32x4 qk(v8 a, v8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+  __device__ static f32x4 pv(i16x4_t a, i16x4_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  __device__ static short pack(float x) { return __builtin_bit_cast(short, static_cast<__bf16>(x)); }
+  __device__ static float unpack(short x) { return __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(x)) << 16); }
+};
+template <> struct Mma<F16> {
+  using v8 = f16x8;
+  __device__ static f32x4 qk(v8 a, v8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+  __device__ static f32x4 pv(i16x4_t a, i16x4_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+  __device__ static short pack(float x) { return __builtin_bit_cast(short, static_cast<_Float16>(x)); }
+  __device__ static float unpack(short x) { return static_cast<float>(__builtin_bit_cast(_Float16, x)); }
+};
+
+__device__ __forceinline__ float swap16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Orders one wave's LDS writes before its own later LDS reads (and vice versa).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+__device__ __forceinline__ int lane_val(int v, int i) { return __builtin_amdgcn_readlane(v, i); }
+
+__device__ __forceinline__ int clamp_ctx(int L, int maxc) { return L < 0 ? 0 : (L > maxc ? maxc : L); }
+
+// Range (within one KV head) whose tiles include tile t: the largest r with r*n/R <= t.
+__device__ __forceinline__ int range_of(int t, int n, int R) {
+  return static_cast<int>(((static_cast<int64_t>(t) + 1) * R - 1) / n);
+}
+
+// Stores 4 fp32 values rounded to the element type as one 8-byte (or 16-byte for fp32) write.
+template <typename T>
+__device__ __forceinline__ void store4(typename T::raw* dst, f32x4 v) {
+  uint2 w;
+  w.x = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_raw(T{}, v[0]))) |
+        (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_raw(T{}, v[1]))) << 16);
+  w.y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_raw(T{}, v[2]))) |
+        (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_raw(T{}, v[3]))) << 16);
+  *reinterpret_cast<uint2*>(dst) = w;
+}
+
+// Per-lane tile entry of tile t (t < T): {physical block, sequence, block index, ntok | kLast}.
+__device__ __forceinline__ int4 tile_entry(const SkParams& p, const int* s_cu, int t) {
+  int a = 0, b = p.num_seqs;  // largest a with cu[a] <= t  (cu[0] = 0 <= t < cu[B] = T)
+  while (b - a > 1) {
+    const int m = (a + b) >> 1;
+    if (s_cu[m] <= t) a = m; else b = m;
+  }
+  const int j = t - s_cu[a];
+  const int nblk = s_cu[a + 1] - s_cu[a];
+  const int L = clamp_ctx(p.context_lens[a], p.max_context_len);
+  const int phys = p.block_tables[static_cast<int64_t>(a) * p.max_blocks_per_seq + j];
+  const int ntok = min(kBlock, L - j * kBlock);
+  return make_int4(phys, a, j, ntok | (j == nblk - 1 ? kLast : 0));
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_sk_kernel(SkParams p) {
+  using M = Mma<T>;
+  using raw = typename T::raw;
+  constexpr int ROW = D * 2;                   // bytes of one head row
+  constexpr int KC = D / 32;                   // QK k-chunks (one 16-byte piece per lane each)
+  constexpr int NC = D / 16;                   // PV output chunks of 16 columns
+  constexpr int PITCH = D == 128 ? 288 : 160;  // LDS row pitch of the V tile: transposing reads hit distinct banks
+  constexpr int TILE_LDS = kBlock * PITCH;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int hgroups = (p.num_kv_heads + kWaves - 1) / kWaves;
+  const int range = blockIdx.x / hgroups;
+  const int g = (blockIdx.x - range * hgroups) * kWaves + wave;
+  const int G = p.group;
+  const int B = p.num_seqs;
+
+  extern __shared__ __attribute__((aligned(16))) int s_dyn[];
+  int* s_cu = s_dyn;                                               // [B + 1]
+  __shared__ __attribute__((aligned(16))) unsigned char s_tile[kWaves][TILE_LDS];
+  __shared__ int s_part[kThreads];
+
+  // ---- prefix sum of block counts (every work-group derives the same list)
+  const int per = (B + kThreads - 1) / kThreads;
+  const int lo = min(B, tid * per), hi = min(B, lo + per);
+  int run = 0;
+  for (int s = lo; s < hi; ++s) {
+    run += (clamp_ctx(p.context_lens[s], p.max_context_len) + kBlock - 1) / kBlock;
+    s_cu[s + 1] = run;
+  }
+  s_part[tid] = run;
+  __syncthreads();
+  for (int o = 1; o < kThreads; o <<= 1) {
+    const int v = tid >= o ? s_part[tid - o] : 0;
+    __syncthreads();
+    s_part[tid] += v;
+    __syncthreads();
+  }
+  const int base = tid > 0 ? s_part[tid - 1] : 0;
+  for (int s = lo; s < hi; ++s) s_cu[s + 1] += base;
+  if (tid == 0) s_cu[0] = 0;
+  __syncthreads();
+  const int ntiles = s_cu[B];
+  if (blockIdx.x == 0) {  // the merge kernel reads the prefix sum and T from here
+    for (int s = tid; s <= B; s += kThreads) p.ws_cu[s] = s_cu[s];
+  }
+  const int t0 = static_cast<int>(static_cast<int64_t>(range) * ntiles / p.ranges);
+  const int t1 = static_cast<int>(static_cast<int64_t>(range + 1) * ntiles / p.ranges);
+  const int n = t1 - t0;
+  if (n <= 0 || g >= p.num_kv_heads) return;  // no barrier follows
+
+  // tile entries: lane i of ent holds tile t0 + kb + i, ent2 the next 64
+  int kb = 0;
+  int4 ent = lane < n ? tile_entry(p, s_cu, t0 + lane) : make_int4(0, 0, 0, 0);
+  int4 ent2 = lane + 64 < n ? tile_entry(p, s_cu, t0 + 64 + lane) : make_int4(0, 0, 0, 0);
+
+  const int64_t block_bytes = static_cast<int64_t>(kBlock) * p.num_kv_heads * ROW;
+  const int voff = r16 * p.num_kv_heads * ROW + g * ROW + grp * 16;
+  const unsigned char* kbase = static_cast<const unsigned char*>(p.k_cache);
+  const unsigned char* vbase = static_cast<const unsigned char*>(p.v_cache);
+  unsigned char* vt = s_tile[wave];
+
+  u32x4 kbuf[KC], vbuf[KC];
+  u32x4 qbuf[KC];
+  int last_s = -1;
+  // Issues the loads of tile kk (a zero-length load when kk is past the range or its block
+  // id is out of the pool); a tile that opens a sequence also brings that sequence's query,
+  // so the query arrives with the first K/V of its segment.
+  auto issue = [&](int kk) {
+    int phys = 0, nrec = 0;
+    if (kk < n) {
+      const int i = kk - kb;
+      phys = i < 64 ? lane_val(ent.x, i) : lane_val(ent2.x, i - 64);
+      const int s = i < 64 ? lane_val(ent.y, i) : lane_val(ent2.y, i - 64);
+      if (s != last_s) {
+        last_s = s;
+        const int h = g * G + (r16 < G ? r16 : 0);
+        const u32x4* qv = reinterpret_cast<const u32x4*>(static_cast<const raw*>(p.q) +
+                                                         (static_cast<int64_t>(s) * p.num_q_heads + h) * D);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) qbuf[c] = qv[grp + 4 * c];
+      }
+      nrec = (phys >= 0 && phys < p.num_blocks) ? static_cast<int>(block_bytes) : 0;
+      phys = nrec ? phys : 0;
+    }
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kbase + phys * block_bytes), 0, nrec, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(vbase + phys * block_bytes), 0, nrec, kRsrcWord3);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) kbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff + c * 64, 0, 0);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) vbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + c * 64, 0, 0);
+  };
+  issue(0);
+
+  int cur_s = -1, seg_j0 = 0, seg_k0 = 0;
+  typename M::v8 qb[KC];
+  float m_run = kNegBig, l_run = 0.f;
+  f32x4 acc[NC];
+  // transposing read of PV chunk n: row 4*grp + (r16 >> 2), columns 16n + 4*(r16 & 3) .. +3
+  const int tr_base = (4 * grp + (r16 >> 2)) * PITCH + 8 * (r16 & 3);
+
+  for (int k = 0; k < n; ++k) {
+    if (k - kb == 64) {  // slide the entry window
+      kb += 64;
+      ent = ent2;
+      ent2 = kb + 64 + lane < n ? tile_entry(p, s_cu, t0 + kb + 64 + lane) : make_int4(0, 0, 0, 0);
+    }
+    const int i = k - kb;
+    const int s = lane_val(ent.y, i), j = lane_val(ent.z, i), fl = lane_val(ent.w, i);
+    const int ntok = fl & 0xff;
+    if (s != cur_s) {  // this tile opens a segment
+      cur_s = s;
+      seg_j0 = j;
+      seg_k0 = k;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) qb[c] = __builtin_bit_cast(typename M::v8, r16 < G ? qbuf[c] : u32x4{0u, 0u, 0u, 0u});
+      m_run = kNegBig;
+      l_run = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // V tile -> LDS (row = token r16), then S^T = K Q^T
+#pragma unroll
+    for (int c = 0; c < KC; ++c) *reinterpret_cast<u32x4*>(vt + r16 * PITCH + (grp + 4 * c) * 16) = vbuf[c];
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) sacc = M::qk(__builtin_bit_cast(typename M::v8, kbuf[c]), qb[c], sacc);
+    issue(k + 1);  // this tile's registers are consumed: the next tile's loads go out now
+
+    // online softmax: lane holds tokens 4*grp + e of head r16
+    float sv[4], mx = kNegBig;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sv[e] = (4 * grp + e < ntok) ? sacc[e] * p.scale_log2e : -INFINITY;
+      mx = fmaxf(mx, sv[e]);
+    }
+    mx = swap32_max(swap16_max(mx));
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
+      const float mn = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      l_run *= alpha;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[c] *= alpha;
+      m_run = mn;
+    }
+    i16x4_t pbits;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const short pe = M::pack(__builtin_amdgcn_exp2f(sv[e] - m_run));
+      pbits[e] = pe;
+      psum += M::unpack(pe);  // the sum uses exactly the rounded weights of the PV product
+    }
+    l_run += psum;
+    wave_lds_sync();
+    if (ntok < kBlock) {  // last block of a sequence: rows past the context may hold anything
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + tr_base + 32 * c));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vb[e] = (4 * grp + e < ntok) ? vb[e] : static_cast<short>(0);
+        acc[c] = M::pv(vb, pbits, acc[c]);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + tr_base + 32 * c));
+        acc[c] = M::pv(vb, pbits, acc[c]);
+      }
+    }
+    wave_lds_sync();
+
+    bool seg_end = (k == n - 1);
+    if (!seg_end) {
+      const int i2 = k + 1 - kb;
+      seg_end = (i2 < 64 ? lane_val(ent.y, i2) : lane_val(ent2.y, i2 - 64)) != s;
+    }
+    if (!seg_end) continue;
+    const float lsum = swap32_sum(swap16_sum(l_run));
+    if (seg_j0 == 0 && (fl & kLast)) {  // the whole sequence lies in this range
+      if (r16 < G) {
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        raw* o = static_cast<raw*>(p.out) + (static_cast<int64_t>(s) * p.num_q_heads + g * G + r16) * D;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) store4<T>(o + 16 * c + 4 * grp, acc[c] * inv);
+      }
+    } else {  // record for the merge kernel: slot 0 = segment that began in an earlier range
+      const int slot = (seg_k0 == 0 && seg_j0 > 0) ? 0 : 1;
+      const int64_t rec = (static_cast<int64_t>(range) * p.num_kv_heads + g) * 2 + slot;
+      float* pa = p.ws_acc + rec * (16 * D);
+      if (r16 < G) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(pa + r16 * D + 16 * c + 4 * grp) = acc[c];
+      }
+      if (grp == 0) *reinterpret_cast<float2*>(p.ws_ml + rec * 32 + r16 * 2) = make_float2(m_run, lsum);
+    }
+    cur_s = -1;
+  }
+}
+
+// Merge of the sequences cut by range boundaries, and zeros for empty sequences.  One
+// work-group of 4 waves per (KV head, sequence): wave v folds in records v, v + 4, ... of the
+// ranges that touched the sequence (two at a time, loads in flight together), then wave 0
+// combines the 4 partial results in a fixed order.  Deterministic.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_sk_kernel(SkParams p) {
+  using raw = typename T::raw;
+  constexpr int NC = D / 16;
+  const int g = blockIdx.x, s = blockIdx.y;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int G = p.group;
+  const int ntiles = p.ws_cu[p.num_seqs];
+  const int c0 = p.ws_cu[s], nblk = p.ws_cu[s + 1] - c0;
+  raw* o = static_cast<raw*>(p.out) + (static_cast<int64_t>(s) * p.num_q_heads + g * G + (r16 < G ? r16 : 0)) * D;
+  if (nblk == 0) {  // empty context: zeros
+    if (wv == 0 && r16 < G) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) store4<T>(o + 16 * c + 4 * grp, f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+    return;
+  }
+  const int ra = range_of(c0, ntiles, p.ranges), rb = range_of(c0 + nblk - 1, ntiles, p.ranges);
+  if (ra == rb) return;  // finished by its range
+  const int nc = rb - ra + 1;
+  const int hr = r16 < G ? r16 : 0;
+  float m = kNegBig, l = 0.f;
+  f32x4 a[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) a[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = wv; c < nc; c += 8) {
+    const bool two = c + 4 < nc;
+    const int64_t r1 = (static_cast<int64_t>(ra + c) * p.num_kv_heads + g) * 2 + (c == 0 ? 1 : 0);
+    const int64_t r2 = two ? (static_cast<int64_t>(ra + c + 4) * p.num_kv_heads + g) * 2 : r1;
+    const float m1 = p.ws_ml[r1 * 32 + r16 * 2], l1 = p.ws_ml[r1 * 32 + r16 * 2 + 1];
+    const float m2 = two ? p.ws_ml[r2 * 32 + r16 * 2] : kNegBig;
+    const float l2 = two ? p.ws_ml[r2 * 32 + r16 * 2 + 1] : 0.f;
+    f32x4 x1[NC], x2[NC];
+#pragma unroll
+    for (int q = 0; q < NC; ++q) x1[q] = *reinterpret_cast<const f32x4*>(p.ws_acc + r1 * (16 * D) + hr * D + 16 * q + 4 * grp);
+#pragma unroll
+    for (int q = 0; q < NC; ++q) x2[q] = *reinterpret_cast<const f32x4*>(p.ws_acc + r2 * (16 * D) + hr * D + 16 * q + 4 * grp);
+    const float mn = fmaxf(m, fmaxf(m1, m2));
+    const float f0 = __builtin_amdgcn_exp2f(m - mn), f1 = __builtin_amdgcn_exp2f(m1 - mn);
+    const float f2 = two ? __builtin_amdgcn_exp2f(m2 - mn) : 0.f;
+    l = l * f0 + l1 * f1 + l2 * f2;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) a[q] = a[q] * f0 + x1[q] * f1 + x2[q] * f2;
+    m = mn;
+  }
+  __shared__ f32x4 s_a[4][NC][64];
+  __shared__ float s_m[4][64], s_l[4][64];
+#pragma unroll
+  for (int q = 0; q < NC; ++q) s_a[wv][q][lane] = a[q];
+  s_m[wv][lane] = m;
+  s_l[wv][lane] = l;
+  __syncthreads();
+  if (wv != 0) return;
+  float Mx = s_m[0][lane];
+#pragma unroll
+  for (int v = 1; v < 4; ++v) Mx = fmaxf(Mx, s_m[v][lane]);
+  float L = 0.f;
+  f32x4 r[NC];
+#pragma unroll
+  for (int q = 0; q < NC; ++q) r[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float f = __builtin_amdgcn_exp2f(s_m[v][lane] - Mx);
+    L = fmaf(s_l[v][lane], f, L);
+#pragma unroll
+    for (int q = 0; q < NC; ++q) r[q] += s_a[v][q][lane] * f;
+  }
+  if (r16 < G) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) store4<T>(o + 16 * q + 4 * grp, r[q] * inv);
+  }
+}
+
+template <typename T, int D>
+hipError_t launch(const SkParams& p, hipStream_t stream) {
+  const int hgroups = (p.num_kv_heads + kWaves - 1) / kWaves;
+  const size_t lds = static_cast<size_t>(p.num_seqs + 1) * sizeof(int);
+  hipLaunchKernelGGL((decode_sk_kernel<T, D>), dim3(p.ranges * hgroups), dim3(kThreads), lds, stream, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((merge_sk_kernel<T, D>), dim3(p.num_kv_heads, p.num_seqs), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+  // About 8 waves per CU on a 256-CU part, and at least 8 tiles per range in the worst case.
+  const int64_t max_blocks = (static_cast<int64_t>(max_context_len) + kBlock - 1) / kBlock;
+  const int64_t upper_tiles = static_cast<int64_t>(num_seqs) * max_blocks;
+  const int32_t hgroups = (num_kv_heads + kWaves - 1) / kWaves;
+  int64_t r = kSkTargetWaves / (static_cast<int64_t>(hgroups) * kWaves);
+  if (r < 1) r = 1;
+  const int64_t cap = (upper_tiles + 7) / 8;
+  if (r > cap) r = cap;
+  return static_cast<int32_t>(r < 1 ? 1 : r);
+}
+
+size_t sk_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len) {
+  const int64_t R = sk_ranges(num_seqs, num_kv_heads, max_context_len);
+  const int64_t recs = R * num_kv_heads * 2;
+  const size_t acc = static_cast<size_t>(recs) * 16 * head_dim * sizeof(float);
+  const size_t ml = static_cast<size_t>(recs) * 32 * sizeof(float);
+  const size_t cu = ((static_cast<size_t>(num_seqs) + 1) * sizeof(int) + 255) / 256 * 256;
+  return acc + ml + cu;
+}
+
+hipError_t sk_launch(SkParams p, int32_t dtype, hipStream_t stream) {
+  const int D = p.head_dim;
+  if (dtype == PKV_BF16) return D == 64 ? launch<BF16, 64>(p, stream) : launch<BF16, 128>(p, stream);
+  return D == 64 ? launch<F16, 64>(p, stream) : launch<F16, 128>(p, stream);
+}
+
+}  // namespace sk
+}  // namespace pkv

@@ -177,17 +177,35 @@ def test_decode_with_no_sequences_is_a_noop():
 def test_workspace_size_and_partition_rules():
     ws = B.paged_attn_workspace_bytes
     ps = B.paged_attn_partition_size
+    # never split / explicit partitions: fixed partitions of that many tokens
     assert ws(256, 64, 8, 128, 8192, -1) == 0
     assert ps(256, 64, 8, 128, 8192, -1) == 8192
     assert ps(4, 4, 4, 64, 100, -1) == 112
     assert ps(8, 32, 8, 128, 32768, 1024) == 1024
     assert ps(8, 32, 8, 128, 32768, 24) == 0
     assert ws(8, 32, 8, 128, 32768, 1024) == 8 * 32 * 32 * 130 * 4
-    auto = ps(256, 64, 8, 128, 8192, 0)
+    # auto with G <= 2: fixed partitions of an automatic size
+    auto = ps(64, 32, 32, 128, 8192, 0)
     assert auto % 16 == 0 and auto > 0
     P = -(-8192 // auto)
-    assert ws(256, 64, 8, 128, 8192, 0) == (0 if P == 1 else 256 * 64 * P * 130 * 4)
+    assert ws(64, 32, 32, 128, 8192, 0) == (0 if P == 1 else 64 * 32 * P * 130 * 4)
     assert ws(4, 4, 4, 64, 100, 0) == 0
+    # auto with G > 2: the even split over the GPU has no fixed partition; its workspace
+    # holds per-range records (16 x D fp32 acc + 16 x 2 stats, two per range and KV head)
+    # plus the prefix sum of block counts
+    assert ps(256, 64, 8, 128, 8192, 0) == 0
+    w128 = ws(256, 64, 8, 128, 8192, 0)
+    w64 = ws(256, 64, 8, 64, 8192, 0)
+    rec128, rec64 = 16 * 128 * 4 + 32 * 4, 16 * 64 * 4 + 32 * 4
+    assert w128 > 0 and (w128 - 257 * 4) // rec128 == (w64 - 257 * 4) // rec64
+    assert ((w128 - 257 * 4) // rec128) % (2 * 8) == 0
+    assert ws(256, 64, 8, 128, 8192, 0) == w128  # deterministic
+    # tiny contexts: at most one range per 8 worst-case tiles
+    assert ws(1, 8, 1, 128, 16, 0) <= 2 * rec128 + 256
+    assert ws(0, 64, 8, 128, 8192, 0) == 0
+    # beyond the even split's batch limit the fixed rule applies again
+    big = ps(9000, 64, 8, 128, 8192, 0)
+    assert big % 16 == 0 and big > 0
 
 
 def test_append_rejects_before_launch():

@@ -114,18 +114,28 @@ def test_shared_prefix_and_copy_give_identical_outputs(variant):
     bt, ctx, maxc = cache.tables(range(5))
     for partition in (0, 64):
         out = decode(cache, q, bt, ctx, maxc, 1.0 / np.sqrt(d), partition)
+        # Fixed partitions treat every sequence alike, so equal inputs give equal bits.  The
+        # even split over the GPU (partition 0 with G > 2) cuts each sequence where the range
+        # boundaries happen to fall, so equal sequences at different batch positions may be
+        # merged in a different grouping: equal up to rounding.
+        exact = partition != 0 or hq // hkv <= 2
         for s in range(1, 5):
-            assert torch.equal(bits(out[s]), bits(out[0])), s
+            if exact:
+                assert torch.equal(bits(out[s]), bits(out[0])), s
+            else:
+                assert float((out[s].double() - out[0].double()).abs().max()) <= TOL[dtype], s
 
 
+@pytest.mark.parametrize("partition", [0, 64])
 @pytest.mark.parametrize("variant", VARIANTS)
-def test_bitwise_deterministic(variant):
-    """I-6: identical inputs give identical bits run to run."""
-    say(f"[inv determinism] {variant}")
+def test_bitwise_deterministic(variant, partition):
+    """I-6: identical inputs give identical bits run to run (no atomics, fixed merge order)."""
+    say(f"[inv determinism] {variant} partition={partition}")
     w = W.Workload(_spec(*variant, (900, 33, 2000, 5)), seed=8)
-    out, cache, bt, ctx, maxc = decode_step(w, partition_size=64)
-    again = decode(cache, w.q, bt, ctx, maxc, w.scale, 64)
-    assert torch.equal(bits(out), bits(again))
+    out, cache, bt, ctx, maxc = decode_step(w, partition_size=partition)
+    for _ in range(2):
+        again = decode(cache, w.q, bt, ctx, maxc, w.scale, partition)
+        assert torch.equal(bits(out), bits(again))
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -134,7 +144,7 @@ def test_split_agrees_with_unsplit(variant):
     say(f"[inv split] {variant}")
     w = W.Workload(_spec(*variant, (1500, 700)), seed=9)
     whole, cache, bt, ctx, maxc = decode_step(w, partition_size=-1)
-    for part in (16, 48, 512):
+    for part in (0, 16, 48, 512):
         split = decode(cache, w.q, bt, ctx, maxc, w.scale, part)
         assert float((split.double() - whole.double()).abs().max()) <= TOL[variant[0]]
 
@@ -161,3 +171,28 @@ def test_nan_canaries_beyond_the_context_are_never_read(variant):
     o3 = decode(cache, w.q, bt, zero_ctx, maxc, w.scale)
     assert torch.equal(o3[1], torch.zeros_like(o3[1]))
     assert torch.equal(bits(o3[0]), bits(out[0]))
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bfloat16", 16, 2, 128), ("float16", 12, 3, 64), ("bfloat16", 40, 5, 128)])
+def test_even_split_edge_cases(dtype, hq, hkv, d):
+    """The even split over the GPU (partition 0, G > 2): every context empty gives zeros; one
+    long sequence cut into many ranges, empty sequences between others, and a KV-head count
+    that is not a multiple of the work-group's 4 heads all match the oracle."""
+    say(f"[split edges] {dtype} Hq={hq} Hkv={hkv} D={d}")
+    tdt = getattr(torch, dtype)
+    rng = np.random.default_rng(12)
+    # all empty
+    cache = PagedKVCache(8, hkv, d, tdt, DEVICE, fill=float("nan"))
+    for s in range(3):
+        cache.add_sequence(s, torch.empty((0, hkv, d), dtype=tdt), torch.empty((0, hkv, d), dtype=tdt))
+    q = torch.from_numpy(rng.standard_normal((3, hq, d), dtype=np.float32)).to(tdt)
+    bt, ctx, maxc = cache.tables(range(3), max_blocks_per_seq=2)
+    out = decode(cache, q, bt, ctx, maxc, 0.1, 0)
+    assert torch.equal(out, torch.zeros_like(out))
+    # mixed: long, empty, short, empty, medium
+    for lens in ((4000, 0, 7, 0, 530), (1, 2, 3, 4097)):
+        w = W.Workload(W.Spec("edges", dtype, len(lens), hq, hkv, d, "fixed", fixed_lengths=lens), seed=13)
+        got, *_ = decode_step(w, partition_size=0)
+        err = max_err(got, oracle_out(w))
+        say(f"    lens={lens}: max abs err {err:.3e}")
+        assert err <= TOL[dtype], err
