@@ -93,6 +93,9 @@ def main():
     ap.add_argument("--config", default="gqa_bf16")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--separate", action="store_true",
+                    help="time the step as two calls (pkv_kv_cache_append, then "
+                         "pkv_paged_attn_decode) instead of one pkv_paged_attn_decode_append")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -144,40 +147,65 @@ def main():
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step():
+    def append_call():
         binding.kv_cache_append(new_k, new_v, cache.k_cache, cache.v_cache, slot_t, stream=stream)
+
+    def decode_call():
         binding.paged_attn_decode(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale,
                                   workspace=ws, partition_size=args.partition, stream=stream)
 
-    log(f"warmup {args.warmup} steps (partition {part} tokens, workspace {ws_bytes} B)")
+    def fused_call():
+        binding.paged_attn_decode_append(out, q, new_k, new_v, cache.k_cache, cache.v_cache, bt, ctx,
+                                         maxc, w.scale, workspace=ws, partition_size=args.partition,
+                                         stream=stream)
+
+    calls = [append_call, decode_call] if args.separate else [fused_call]
+    log(f"warmup {args.warmup} steps ({'append + decode' if args.separate else 'fused append+decode'}, "
+        f"partition {part or 'even split'}, workspace {ws_bytes} B)")
     for _ in range(args.warmup):
-        step()
+        for c in calls:
+            c()
     torch.cuda.synchronize()
 
+    # Timed region: K steps back to back, bracketed by synchronize + events on the launch stream.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(K):
-        ev[i][0].record(stream)
-        binding.kv_cache_append(new_k, new_v, cache.k_cache, cache.v_cache, slot_t, stream=stream)
-        ev[i][1].record(stream)
-        binding.paged_attn_decode(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale,
-                                  workspace=ws, partition_size=args.partition, stream=stream)
-        ev[i][2].record(stream)
+    for _ in range(K):
+        for c in calls:
+            c()
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    t_app = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
-    t_dec = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
     ms_step = total_ms / K
-    log(f"step {ms_step * 1e3:.1f} us: append {t_app.mean() * 1e3:.1f} us, decode "
-        f"median {np.median(t_dec) * 1e3:.1f} us (p10 {np.percentile(t_dec, 10) * 1e3:.1f}, "
-        f"p90 {np.percentile(t_dec, 90) * 1e3:.1f})")
+    # Per-call durations for the roofline record: a second pass of K steps with HIP events on
+    # the launch stream around every call (kept out of the step timing above).
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev[i][0].record(stream)
+        for j, c in enumerate(calls):
+            c()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    t_calls = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(len(calls))] for i in range(K)])
+    t_dec = t_calls[:, -1]
+    t_app = t_calls[:, 0] if args.separate else None
+    if args.separate:
+        log(f"step {ms_step * 1e3:.1f} us: append {t_app.mean() * 1e3:.1f} us, decode "
+            f"median {np.median(t_dec) * 1e3:.1f} us (p10 {np.percentile(t_dec, 10) * 1e3:.1f}, "
+            f"p90 {np.percentile(t_dec, 90) * 1e3:.1f})")
+    else:
+        log(f"step {ms_step * 1e3:.1f} us: fused append+decode call median {np.median(t_dec) * 1e3:.1f} us "
+            f"(p10 {np.percentile(t_dec, 10) * 1e3:.1f}, p90 {np.percentile(t_dec, 90) * 1e3:.1f})")
 
     kv_bytes, dec_bytes = algorithmic_bytes(w)
+    e_bytes = {"float32": 4, "float16": 2, "bfloat16": 2}[sp.dtype]
+    app_bytes = 4 * sp.num_seqs * sp.num_kv_heads * sp.head_dim * e_bytes  # new rows read + written
+    if not args.separate:
+        dec_bytes += app_bytes
     dec_s = float(t_dec.mean()) / 1e3
     gbs = kv_bytes / (ms_step / 1e3) / 1e9
     achieved = dec_bytes / dec_s / 1e9
@@ -207,8 +235,10 @@ def main():
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s_per_layer": round(sp.num_seqs / (ms_step / 1e3), 1),
         "decode_tokens_per_s_70b_shape_attention_only": round(sp.num_seqs / (LAYERS_70B * ms_step / 1e3), 1),
-        "append_us": round(float(t_app.mean()) * 1e3, 2),
+        "append_us": None if t_app is None else round(float(t_app.mean()) * 1e3, 2),
         "decode_us_median": round(float(np.median(t_dec)) * 1e3, 2),
+        "step_calls": "pkv_kv_cache_append + pkv_paged_attn_decode" if args.separate
+                      else "pkv_paged_attn_decode_append (append fused into the decode)",
         "config": {
             "workload": f"{sp.name}: paged decode, B={sp.num_seqs}, Hq={sp.num_q_heads}, "
                         f"Hkv={sp.num_kv_heads}, D={sp.head_dim}, block 16, {sp.dtype}, "
@@ -220,7 +250,8 @@ def main():
             "pool_blocks": w.num_blocks,
         },
         "roofline": {
-            "kernel": "pkv_paged_attn_decode (decode kernel + merge of split sequences)",
+            "kernel": ("pkv_paged_attn_decode" if args.separate else "pkv_paged_attn_decode_append") +
+                      " (decode kernel + merge of sequences cut by the split)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

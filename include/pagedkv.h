@@ -111,16 +111,25 @@ PKV_API pkv_status pkv_kv_cache_append(const void* key, const void* value,
 /* Device: paged decode attention                                                        */
 /* ------------------------------------------------------------------------------------ */
 
-/* Bytes of fp32 workspace pkv_paged_attn_decode needs for these arguments (0 when the
- * chosen partitioning does not split any sequence).  partition_size as for the decode
- * call. Returns 0 for arguments the decode call would reject. */
+/* Bytes of workspace pkv_paged_attn_decode needs for these arguments (0 when the chosen
+ * work split needs none), partition_size as for the decode call.
+ *   - partition_size 0 with grouped queries (num_q_heads / num_kv_heads > 2) and at most 8192
+ *     sequences: the even split over the GPU; the workspace holds fp32 records of sequences cut
+ *     by the split (two per work range and KV head, 16*head_dim + 32 floats each) and the
+ *     prefix sum of block counts; it does not depend on the dtype or on the context lengths
+ *     beyond max_context_len.
+ *   - otherwise: fixed partitions; fp32 partials of split sequences,
+ *     num_seqs * num_q_heads * P * (head_dim + 2) floats with P partitions of the longest
+ *     context, 0 when nothing is split.
+ * Returns 0 for arguments the decode call would reject. */
 PKV_API size_t pkv_paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim,
                                       int32_t max_context_len, int32_t partition_size);
 
-/* The partition size (tokens) pkv_paged_attn_decode will use for these arguments:
- * the resolved value of partition_size 0 (auto) or -1 (never split: max_context_len
- * rounded up to the block size), or partition_size itself.  0 on invalid arguments. */
+/* The fixed partition size (tokens) pkv_paged_attn_decode uses for these arguments: the
+ * resolved value of partition_size 0 (auto) or -1 (never split: max_context_len rounded up
+ * to the block size), or partition_size itself.  0 when the even split over the GPU is used
+ * (partition_size 0 with grouped queries, see above) and on invalid arguments. */
 PKV_API int32_t pkv_paged_attn_partition_size(int32_t num_seqs, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim,
                                       int32_t max_context_len, int32_t partition_size);
@@ -146,15 +155,22 @@ PKV_API int32_t pkv_paged_attn_partition_size(int32_t num_seqs, int32_t num_q_he
  *   context_lens   device int32 [num_seqs]
  *   max_context_len host int, >= every context_lens[s], <= max_blocks_per_seq*block_size
  *   scale          logit scale (usually 1/sqrt(head_dim))
- *   workspace      device fp32 scratch of >= pkv_paged_attn_workspace_bytes(...) bytes
- *                  (may be NULL when that is 0); contents on return unspecified
+ *   workspace      device scratch of >= pkv_paged_attn_workspace_bytes(...) bytes, 16-byte
+ *                  aligned (may be NULL when that is 0); contents on entry and return
+ *                  unspecified (no state carries over between calls)
  *   partition_size 0 = auto; -1 = never split; else tokens per partition, a positive
- *                  multiple of block_size.  Sequences longer than one partition are
- *                  processed as independent partitions and merged exactly (log-sum-exp
- *                  combine in a fixed order), so the result is deterministic.
+ *                  multiple of block_size.  With 0 and grouped queries (num_q_heads /
+ *                  num_kv_heads > 2, f16/bf16, at most 8192 sequences) the work is split
+ *                  evenly over the GPU: each KV head's list of (sequence, block) tiles is cut
+ *                  into equal ranges whatever the length mix, and sequences cut by the ranges
+ *                  are merged exactly (log-sum-exp combine in a fixed order) by a second
+ *                  kernel.  Otherwise sequences longer than one partition are processed as
+ *                  independent partitions and merged the same way.
  *
  * A sequence with context length 0 yields zeros.  Results are bitwise reproducible run to
- * run for identical inputs and arguments.
+ * run for identical inputs and arguments (no atomics; every merge has a fixed order).  With
+ * the even split, two sequences with equal contents at different batch positions may be cut
+ * differently and then agree up to rounding rather than bit for bit.
  * Device-side contract (not checked on the host): context_lens[s] in [0, max_context_len]
  * and table entries in [0, num_blocks).  To never touch memory outside the buffers, the
  * kernels clamp context lengths to max_context_len and skip blocks whose id is out of
@@ -170,6 +186,35 @@ PKV_API pkv_status pkv_paged_attn_decode(void* out, const void* q,
                                  int32_t num_seqs, int32_t num_q_heads, float scale,
                                  void* workspace, size_t workspace_bytes,
                                  int32_t partition_size, void* stream);
+
+/* One decode step in one call: the KV append of each sequence's new token, then the decode
+ * of pkv_paged_attn_decode over contexts that include it.
+ *
+ * The new token of sequence s is its last one, position context_lens[s] - 1, whose slot the
+ * block table gives (block block_tables[s][(ctx-1)/bs], offset (ctx-1) % bs): the append step
+ * of [111cn] §3.3 after the host pool has taken that slot (pkv_seq_extend by one token).
+ * The result equals pkv_kv_cache_append with those slots followed by pkv_paged_attn_decode,
+ * bit for bit in the pools and in the output.  On the evenly split path the wave that
+ * reads a sequence's last block takes the new row from new_key/new_value and writes it to
+ * the pool itself, so the step is one decode launch plus the merge; otherwise a scatter
+ * launch precedes the decode.
+ *
+ *   new_key, new_value  device [num_seqs][num_kv_heads][head_dim] of cache->dtype, 16-byte
+ *                       aligned, read only
+ *   k_cache, v_cache    written at the new tokens' slots, read everywhere else
+ *   all other arguments as for pkv_paged_attn_decode (max_blocks_per_seq must be > 0)
+ * Sequences with context length 0 append nothing.  Block ids outside the pool are skipped
+ * for the write as for the read.  Errors: as pkv_paged_attn_decode, plus INVALID_ARGUMENT
+ * for missing or misaligned new_key/new_value. */
+PKV_API pkv_status pkv_paged_attn_decode_append(void* out, const void* q,
+                                        const void* new_key, const void* new_value,
+                                        void* k_cache, void* v_cache,
+                                        const pkv_cache_desc* cache,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t max_context_len,
+                                        int32_t num_seqs, int32_t num_q_heads, float scale,
+                                        void* workspace, size_t workspace_bytes,
+                                        int32_t partition_size, void* stream);
 
 /* ------------------------------------------------------------------------------------ */
 /* Host: block pool and block tables                                                     */

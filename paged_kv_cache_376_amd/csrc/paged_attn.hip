@@ -35,6 +35,7 @@
 #include <cmath>
 #include <type_traits>
 
+#include "device_launch.h"
 #include "dtypes.h"
 #include "pkv_internal.h"
 #include "stream_k.h"
@@ -577,14 +578,19 @@ extern "C" size_t pkv_paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q
   return static_cast<size_t>(num_seqs) * num_q_heads * P * (static_cast<size_t>(head_dim) + 2) * sizeof(float);
 }
 
-extern "C" pkv_status pkv_paged_attn_decode(void* out, const void* q, const void* k_cache,
-                                            const void* v_cache, const pkv_cache_desc* cache,
-                                            const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                            const int32_t* context_lens, int32_t max_context_len,
-                                            int32_t num_seqs, int32_t num_q_heads, float scale,
-                                            void* workspace, size_t workspace_bytes,
-                                            int32_t partition_size, void* stream) {
+namespace {
+
+// Shared body of the two decode entry points.  With new_key/new_value set, each sequence's
+// last token first gets its new K/V row (inside the decode kernel on the evenly split path,
+// by a separate scatter launch otherwise).
+pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const pkv_cache_desc* cache, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, float scale,
+                       void* workspace, size_t workspace_bytes, int32_t partition_size, void* stream,
+                       const void* new_key, const void* new_value) {
   clear_error();
+  const bool append = new_key != nullptr || new_value != nullptr;
   if (!cache) return fail(PKV_ERR_INVALID_ARGUMENT, "cache descriptor is NULL");
   const int e = dtype_bytes(cache->dtype);
   if (e == 0) return fail(PKV_ERR_UNSUPPORTED, "dtype %d", cache->dtype);
@@ -616,6 +622,10 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, const void* q, const void
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
       (reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
     return fail(PKV_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  if (append && (!new_key || !new_value || !aligned16(new_key) || !aligned16(new_value)))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "new_key and new_value must both be 16-byte aligned device pointers");
+  if (append && max_blocks_per_seq == 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "an append needs a block table (max_blocks_per_seq > 0)");
   if (sk_path) {
     if (cache->dtype == PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "group size %d needs f16/bf16", G);
     const size_t need = sk::sk_workspace_bytes(num_seqs, cache->num_kv_heads, D, max_context_len);
@@ -625,8 +635,10 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, const void* q, const void
     sk::SkParams sp;
     sp.out = out;
     sp.q = q;
-    sp.k_cache = k_cache;
-    sp.v_cache = v_cache;
+    sp.k_cache = const_cast<void*>(k_cache);  // written only when appending (pools are then the caller's writable ones)
+    sp.v_cache = const_cast<void*>(v_cache);
+    sp.new_key = new_key;
+    sp.new_value = new_value;
     sp.block_tables = block_tables;
     sp.context_lens = context_lens;
     sp.num_seqs = num_seqs;
@@ -678,6 +690,11 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, const void* q, const void
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
+  if (append) {
+    err = launch_append_last(new_key, new_value, const_cast<void*>(k_cache), const_cast<void*>(v_cache), cache,
+                             block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs, st);
+    if (err != hipSuccess) return fail(PKV_ERR_HIP, "append launch: %s", hipGetErrorString(err));
+  }
   switch (cache->dtype) {
     case PKV_F32: err = launch_dtype<F32>(p, D, G, st); break;
     case PKV_F16: err = launch_dtype<F16>(p, D, G, st); break;
@@ -685,4 +702,35 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, const void* q, const void
   }
   if (err != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_paged_attn_decode(void* out, const void* q, const void* k_cache,
+                                            const void* v_cache, const pkv_cache_desc* cache,
+                                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                            const int32_t* context_lens, int32_t max_context_len,
+                                            int32_t num_seqs, int32_t num_q_heads, float scale,
+                                            void* workspace, size_t workspace_bytes,
+                                            int32_t partition_size, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, cache, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, num_seqs, num_q_heads, scale, workspace, workspace_bytes,
+                     partition_size, stream, nullptr, nullptr);
+}
+
+extern "C" pkv_status pkv_paged_attn_decode_append(void* out, const void* q, const void* new_key,
+                                                   const void* new_value, void* k_cache, void* v_cache,
+                                                   const pkv_cache_desc* cache,
+                                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                   const int32_t* context_lens, int32_t max_context_len,
+                                                   int32_t num_seqs, int32_t num_q_heads, float scale,
+                                                   void* workspace, size_t workspace_bytes,
+                                                   int32_t partition_size, void* stream) {
+  if (!new_key || !new_value) {
+    clear_error();
+    return fail(PKV_ERR_INVALID_ARGUMENT, "new_key and new_value must not be NULL");
+  }
+  return decode_impl(out, q, k_cache, v_cache, cache, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, num_seqs, num_q_heads, scale, workspace, workspace_bytes,
+                     partition_size, stream, new_key, new_value);
 }

@@ -44,7 +44,11 @@ namespace sk {
 namespace {
 
 constexpr int kBlock = 16;
-constexpr int kWaves = 4;                 // KV heads (waves) per work-group
+// Work-group shape: kHeads KV heads side by side (their waves read neighbouring slices of the
+// same token rows together) x kSplits consecutive sub-ranges of the tile list (merged in LDS).
+constexpr int kHeads = 4;
+constexpr int kSplits = 2;
+constexpr int kWaves = kHeads * kSplits;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kNegBig = -1.0e30f;
 constexpr float kTau = 8.0f;              // lazy-rescale threshold (log2 units)
@@ -131,6 +135,17 @@ __device__ __forceinline__ int4 tile_entry(const SkParams& p, const int* s_cu, i
   return make_int4(phys, a, j, ntok | (j == nblk - 1 ? kLast : 0));
 }
 
+// LDS layout of the decode kernel (dynamic): the prefix sum of block counts, then one region
+// that holds the 4 waves' V tiles during the tile loop and the 8 wave states after it.
+__host__ __device__ constexpr int sk_pitch(int D) { return D == 128 ? 288 : 160; }
+__host__ __device__ inline int sk_state_bytes(int D, int G) { return ((D / 16) * 4 * G * 16 + G * 8 + 15) / 16 * 16; }
+__host__ __device__ inline int sk_cu_bytes(int B) { return ((B + 1) * 4 + 15) / 16 * 16; }
+__host__ __device__ inline int sk_lds_bytes(int B, int D, int G) {
+  const int tiles = kWaves * kBlock * sk_pitch(D);
+  const int states = 2 * kWaves * sk_state_bytes(D, G);
+  return sk_cu_bytes(B) + (tiles > states ? tiles : states);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_sk_kernel(SkParams p) {
@@ -139,22 +154,28 @@ void decode_sk_kernel(SkParams p) {
   constexpr int ROW = D * 2;                   // bytes of one head row
   constexpr int KC = D / 32;                   // QK k-chunks (one 16-byte piece per lane each)
   constexpr int NC = D / 16;                   // PV output chunks of 16 columns
-  constexpr int PITCH = D == 128 ? 288 : 160;  // LDS row pitch of the V tile: transposing reads hit distinct banks
+  constexpr int PITCH = sk_pitch(D);           // V tile row pitch: the transposing reads hit distinct banks
   constexpr int TILE_LDS = kBlock * PITCH;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
-  const int hgroups = (p.num_kv_heads + kWaves - 1) / kWaves;
-  const int range = blockIdx.x / hgroups;
-  const int g = (blockIdx.x - range * hgroups) * kWaves + wave;
+  // wave = (split sw, head column hw); head groups innermost so that all heads of one range
+  // are dispatched together
+  const int hw = wave % kHeads, sw = wave / kHeads;
+  const int hgroups = (p.num_kv_heads + kHeads - 1) / kHeads;
+  const int hg = blockIdx.x % hgroups;
+  const int wgr = blockIdx.x / hgroups;
+  const int g = hg * kHeads + hw;
+  const bool head_ok = g < p.num_kv_heads;
   const int G = p.group;
   const int B = p.num_seqs;
 
-  extern __shared__ __attribute__((aligned(16))) int s_dyn[];
-  int* s_cu = s_dyn;                                               // [B + 1]
-  __shared__ __attribute__((aligned(16))) unsigned char s_tile[kWaves][TILE_LDS];
+  extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
+  int* s_cu = reinterpret_cast<int*>(s_dyn);                  // [B + 1]
+  unsigned char* s_work = s_dyn + sk_cu_bytes(B);              // V tiles, later wave states
   __shared__ int s_part[kThreads];
+  __shared__ int s_flags[kWaves][5];
 
   // ---- prefix sum of block counts (every work-group derives the same list)
   const int per = (B + kThreads - 1) / kThreads;
@@ -177,163 +198,288 @@ void decode_sk_kernel(SkParams p) {
   if (tid == 0) s_cu[0] = 0;
   __syncthreads();
   const int ntiles = s_cu[B];
-  if (blockIdx.x == 0) {  // the merge kernel reads the prefix sum and T from here
+  if (blockIdx.x == 0) {  // the merge kernel reads the prefix sum from here
     for (int s = tid; s <= B; s += kThreads) p.ws_cu[s] = s_cu[s];
   }
-  const int t0 = static_cast<int>(static_cast<int64_t>(range) * ntiles / p.ranges);
-  const int t1 = static_cast<int>(static_cast<int64_t>(range + 1) * ntiles / p.ranges);
-  const int n = t1 - t0;
-  if (n <= 0 || g >= p.num_kv_heads) return;  // no barrier follows
+  // this work-group's range of the head's tile list, and this wave's sub-range of it
+  const int T0 = static_cast<int>(static_cast<int64_t>(wgr) * ntiles / p.ranges);
+  const int T1 = static_cast<int>(static_cast<int64_t>(wgr + 1) * ntiles / p.ranges);
+  const int t0 = T0 + static_cast<int>(static_cast<int64_t>(T1 - T0) * sw / kSplits);
+  const int t1 = T0 + static_cast<int>(static_cast<int64_t>(T1 - T0) * (sw + 1) / kSplits);
+  const int n = head_ok ? t1 - t0 : 0;
 
-  // tile entries: lane i of ent holds tile t0 + kb + i, ent2 the next 64
-  int kb = 0;
-  int4 ent = lane < n ? tile_entry(p, s_cu, t0 + lane) : make_int4(0, 0, 0, 0);
-  int4 ent2 = lane + 64 < n ? tile_entry(p, s_cu, t0 + 64 + lane) : make_int4(0, 0, 0, 0);
-
-  const int64_t block_bytes = static_cast<int64_t>(kBlock) * p.num_kv_heads * ROW;
-  const int voff = r16 * p.num_kv_heads * ROW + g * ROW + grp * 16;
-  const unsigned char* kbase = static_cast<const unsigned char*>(p.k_cache);
-  const unsigned char* vbase = static_cast<const unsigned char*>(p.v_cache);
-  unsigned char* vt = s_tile[wave];
-
-  u32x4 kbuf[KC], vbuf[KC];
-  u32x4 qbuf[KC];
-  int last_s = -1;
-  // Issues the loads of tile kk (a zero-length load when kk is past the range or its block
-  // id is out of the pool); a tile that opens a sequence also brings that sequence's query,
-  // so the query arrives with the first K/V of its segment.
-  auto issue = [&](int kk) {
-    int phys = 0, nrec = 0;
-    if (kk < n) {
-      const int i = kk - kb;
-      phys = i < 64 ? lane_val(ent.x, i) : lane_val(ent2.x, i - 64);
-      const int s = i < 64 ? lane_val(ent.y, i) : lane_val(ent2.y, i - 64);
-      if (s != last_s) {
-        last_s = s;
-        const int h = g * G + (r16 < G ? r16 : 0);
-        const u32x4* qv = reinterpret_cast<const u32x4*>(static_cast<const raw*>(p.q) +
-                                                         (static_cast<int64_t>(s) * p.num_q_heads + h) * D);
-#pragma unroll
-        for (int c = 0; c < KC; ++c) qbuf[c] = qv[grp + 4 * c];
-      }
-      nrec = (phys >= 0 && phys < p.num_blocks) ? static_cast<int>(block_bytes) : 0;
-      phys = nrec ? phys : 0;
-    }
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kbase + phys * block_bytes), 0, nrec, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(vbase + phys * block_bytes), 0, nrec, kRsrcWord3);
-#pragma unroll
-    for (int c = 0; c < KC; ++c) kbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff + c * 64, 0, 0);
-#pragma unroll
-    for (int c = 0; c < KC; ++c) vbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + c * 64, 0, 0);
-  };
-  issue(0);
-
-  int cur_s = -1, seg_j0 = 0, seg_k0 = 0;
-  typename M::v8 qb[KC];
+  // state of the segment that began before this wave (A) and of the one that runs past its end (Z)
+  bool hasA = false, a_through = false, hasZ = false;
+  int sA = -1, sZ = -1;
+  float mA = kNegBig, lA = 0.f, lZ = 0.f;
+  f32x4 accA[NC];
   float m_run = kNegBig, l_run = 0.f;
   f32x4 acc[NC];
-  // transposing read of PV chunk n: row 4*grp + (r16 >> 2), columns 16n + 4*(r16 & 3) .. +3
-  const int tr_base = (4 * grp + (r16 >> 2)) * PITCH + 8 * (r16 & 3);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) { accA[c] = f32x4{0.f, 0.f, 0.f, 0.f}; acc[c] = accA[c]; }
 
-  for (int k = 0; k < n; ++k) {
-    if (k - kb == 64) {  // slide the entry window
-      kb += 64;
-      ent = ent2;
-      ent2 = kb + 64 + lane < n ? tile_entry(p, s_cu, t0 + kb + 64 + lane) : make_int4(0, 0, 0, 0);
-    }
-    const int i = k - kb;
-    const int s = lane_val(ent.y, i), j = lane_val(ent.z, i), fl = lane_val(ent.w, i);
-    const int ntok = fl & 0xff;
-    if (s != cur_s) {  // this tile opens a segment
-      cur_s = s;
-      seg_j0 = j;
-      seg_k0 = k;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) qb[c] = __builtin_bit_cast(typename M::v8, r16 < G ? qbuf[c] : u32x4{0u, 0u, 0u, 0u});
-      m_run = kNegBig;
-      l_run = 0.f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // V tile -> LDS (row = token r16), then S^T = K Q^T
-#pragma unroll
-    for (int c = 0; c < KC; ++c) *reinterpret_cast<u32x4*>(vt + r16 * PITCH + (grp + 4 * c) * 16) = vbuf[c];
-    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < KC; ++c) sacc = M::qk(__builtin_bit_cast(typename M::v8, kbuf[c]), qb[c], sacc);
-    issue(k + 1);  // this tile's registers are consumed: the next tile's loads go out now
+  if (n > 0) {
+    // tile entries: lane i of ent holds tile t0 + kb + i, ent2 the next 64
+    int kb = 0;
+    int4 ent = lane < n ? tile_entry(p, s_cu, t0 + lane) : make_int4(0, 0, 0, 0);
+    int4 ent2 = lane + 64 < n ? tile_entry(p, s_cu, t0 + 64 + lane) : make_int4(0, 0, 0, 0);
 
-    // online softmax: lane holds tokens 4*grp + e of head r16
-    float sv[4], mx = kNegBig;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sv[e] = (4 * grp + e < ntok) ? sacc[e] * p.scale_log2e : -INFINITY;
-      mx = fmaxf(mx, sv[e]);
-    }
-    mx = swap32_max(swap16_max(mx));
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
-      const float mn = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-      l_run *= alpha;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) acc[c] *= alpha;
-      m_run = mn;
-    }
-    i16x4_t pbits;
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const short pe = M::pack(__builtin_amdgcn_exp2f(sv[e] - m_run));
-      pbits[e] = pe;
-      psum += M::unpack(pe);  // the sum uses exactly the rounded weights of the PV product
-    }
-    l_run += psum;
-    wave_lds_sync();
-    if (ntok < kBlock) {  // last block of a sequence: rows past the context may hold anything
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + tr_base + 32 * c));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vb[e] = (4 * grp + e < ntok) ? vb[e] : static_cast<short>(0);
-        acc[c] = M::pv(vb, pbits, acc[c]);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + tr_base + 32 * c));
-        acc[c] = M::pv(vb, pbits, acc[c]);
-      }
-    }
-    wave_lds_sync();
+    const int64_t block_bytes = static_cast<int64_t>(kBlock) * p.num_kv_heads * ROW;
+    const int voff = r16 * p.num_kv_heads * ROW + g * ROW + grp * 16;
+    unsigned char* kbase = static_cast<unsigned char*>(p.k_cache);
+    unsigned char* vbase = static_cast<unsigned char*>(p.v_cache);
+    unsigned char* vt = s_work + wave * TILE_LDS;
+    const bool append = p.new_key != nullptr;
 
-    bool seg_end = (k == n - 1);
-    if (!seg_end) {
-      const int i2 = k + 1 - kb;
-      seg_end = (i2 < 64 ? lane_val(ent.y, i2) : lane_val(ent2.y, i2 - 64)) != s;
-    }
-    if (!seg_end) continue;
-    const float lsum = swap32_sum(swap16_sum(l_run));
-    if (seg_j0 == 0 && (fl & kLast)) {  // the whole sequence lies in this range
-      if (r16 < G) {
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        raw* o = static_cast<raw*>(p.out) + (static_cast<int64_t>(s) * p.num_q_heads + g * G + r16) * D;
+    u32x4 kbuf[KC], vbuf[KC], qbuf[KC], nk[KC], nv[KC];
+    int last_s = -1;
+    // Issues the loads of tile kk (a zero-length load when kk is past the range or its block
+    // id is outside the pool).  A tile that opens a sequence also brings that sequence's
+    // query; with a fused append, the last tile of a sequence also brings its new K/V row.
+    auto issue = [&](int kk) {
+      int phys = 0, nrec = 0;
+      if (kk < n) {
+        const int i = kk - kb;
+        phys = i < 64 ? lane_val(ent.x, i) : lane_val(ent2.x, i - 64);
+        const int s = i < 64 ? lane_val(ent.y, i) : lane_val(ent2.y, i - 64);
+        const int fl = i < 64 ? lane_val(ent.w, i) : lane_val(ent2.w, i - 64);
+        if (s != last_s) {
+          last_s = s;
+          const int h = g * G + (r16 < G ? r16 : 0);
+          const u32x4* qv = reinterpret_cast<const u32x4*>(static_cast<const raw*>(p.q) +
+                                                           (static_cast<int64_t>(s) * p.num_q_heads + h) * D);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) store4<T>(o + 16 * c + 4 * grp, acc[c] * inv);
-      }
-    } else {  // record for the merge kernel: slot 0 = segment that began in an earlier range
-      const int slot = (seg_k0 == 0 && seg_j0 > 0) ? 0 : 1;
-      const int64_t rec = (static_cast<int64_t>(range) * p.num_kv_heads + g) * 2 + slot;
-      float* pa = p.ws_acc + rec * (16 * D);
-      if (r16 < G) {
+          for (int c = 0; c < KC; ++c) qbuf[c] = qv[grp + 4 * c];
+        }
+        if (append && (fl & kLast)) {
+          const int64_t row = (static_cast<int64_t>(s) * p.num_kv_heads + g) * D;
+          const u32x4* kn = reinterpret_cast<const u32x4*>(static_cast<const raw*>(p.new_key) + row);
+          const u32x4* vn = reinterpret_cast<const u32x4*>(static_cast<const raw*>(p.new_value) + row);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(pa + r16 * D + 16 * c + 4 * grp) = acc[c];
+          for (int c = 0; c < KC; ++c) { nk[c] = kn[grp + 4 * c]; nv[c] = vn[grp + 4 * c]; }
+        }
+        nrec = (phys >= 0 && phys < p.num_blocks) ? static_cast<int>(block_bytes) : 0;
+        phys = nrec ? phys : 0;
       }
-      if (grp == 0) *reinterpret_cast<float2*>(p.ws_ml + rec * 32 + r16 * 2) = make_float2(m_run, lsum);
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(kbase + phys * block_bytes, 0, nrec, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(vbase + phys * block_bytes, 0, nrec, kRsrcWord3);
+#pragma unroll
+      for (int c = 0; c < KC; ++c) kbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff + c * 64, 0, 0);
+#pragma unroll
+      for (int c = 0; c < KC; ++c) vbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + c * 64, 0, 0);
+    };
+    issue(0);
+
+    int cur_s = -1, seg_j0 = 0, seg_k0 = 0;
+    typename M::v8 qb[KC];
+    // transposing read of PV chunk c: row 4*grp + (r16 >> 2), columns 16c + 4*(r16 & 3) .. +3
+    const int tr_base = (4 * grp + (r16 >> 2)) * PITCH + 8 * (r16 & 3);
+
+    for (int k = 0; k < n; ++k) {
+      if (k - kb == 64) {  // slide the entry window
+        kb += 64;
+        ent = ent2;
+        ent2 = kb + 64 + lane < n ? tile_entry(p, s_cu, t0 + kb + 64 + lane) : make_int4(0, 0, 0, 0);
+      }
+      const int i = k - kb;
+      const int s = lane_val(ent.y, i), j = lane_val(ent.z, i), fl = lane_val(ent.w, i);
+      const int ntok = fl & 0xff;
+      if (s != cur_s) {  // this tile opens a segment
+        cur_s = s;
+        seg_j0 = j;
+        seg_k0 = k;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) qb[c] = __builtin_bit_cast(typename M::v8, r16 < G ? qbuf[c] : u32x4{0u, 0u, 0u, 0u});
+        m_run = kNegBig;
+        l_run = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      if (append && (fl & kLast)) {
+        // the sequence's new token is its last one (row ntok - 1 of this block): use the new
+        // row and write it to its pool slot
+        const bool mine = r16 == ntok - 1;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          kbuf[c] = mine ? nk[c] : kbuf[c];
+          vbuf[c] = mine ? nv[c] : vbuf[c];
+        }
+        const int phys = lane_val(ent.x, i);
+        if (mine && phys >= 0 && phys < p.num_blocks) {
+#pragma unroll
+          for (int c = 0; c < KC; ++c) {
+            *reinterpret_cast<u32x4*>(kbase + phys * block_bytes + voff + c * 64) = kbuf[c];
+            *reinterpret_cast<u32x4*>(vbase + phys * block_bytes + voff + c * 64) = vbuf[c];
+          }
+        }
+      }
+      // V tile -> LDS (row = token r16), then S^T = K Q^T
+#pragma unroll
+      for (int c = 0; c < KC; ++c) *reinterpret_cast<u32x4*>(vt + r16 * PITCH + (grp + 4 * c) * 16) = vbuf[c];
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) sacc = M::qk(__builtin_bit_cast(typename M::v8, kbuf[c]), qb[c], sacc);
+      issue(k + 1);  // this tile's registers are consumed: the next tile's loads go out now
+
+      // online softmax: lane holds tokens 4*grp + e of head r16
+      float sv[4], mx = kNegBig;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sv[e] = (4 * grp + e < ntok) ? sacc[e] * p.scale_log2e : -INFINITY;
+        mx = fmaxf(mx, sv[e]);
+      }
+      mx = swap32_max(swap16_max(mx));
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
+        const float mn = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+        l_run *= alpha;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[c] *= alpha;
+        m_run = mn;
+      }
+      i16x4_t pbits;
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const short pe = M::pack(__builtin_amdgcn_exp2f(sv[e] - m_run));
+        pbits[e] = pe;
+        psum += M::unpack(pe);  // the sum uses exactly the rounded weights of the PV product
+      }
+      l_run += psum;
+      wave_lds_sync();
+      if (ntok < kBlock) {  // last block of a sequence: rows past the context may hold anything
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + tr_base + 32 * c));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vb[e] = (4 * grp + e < ntok) ? vb[e] : static_cast<short>(0);
+          acc[c] = M::pv(vb, pbits, acc[c]);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + tr_base + 32 * c));
+          acc[c] = M::pv(vb, pbits, acc[c]);
+        }
+      }
+      wave_lds_sync();
+
+      bool seg_end = (k == n - 1);
+      if (!seg_end) {
+        const int i2 = k + 1 - kb;
+        seg_end = (i2 < 64 ? lane_val(ent.y, i2) : lane_val(ent2.y, i2 - 64)) != s;
+      }
+      if (!seg_end) continue;
+      const float lsum = swap32_sum(swap16_sum(l_run));
+      if (seg_j0 == 0 && (fl & kLast)) {  // the whole sequence lies in this wave's sub-range
+        if (r16 < G) {
+          const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+          raw* o = static_cast<raw*>(p.out) + (static_cast<int64_t>(s) * p.num_q_heads + g * G + r16) * D;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) store4<T>(o + 16 * c + 4 * grp, acc[c] * inv);
+        }
+      } else if (seg_k0 == 0 && seg_j0 > 0) {  // began in an earlier sub-range (A)
+        hasA = true;
+        a_through = !(fl & kLast);
+        sA = s;
+        mA = m_run;
+        lA = lsum;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) accA[c] = acc[c];
+      } else {  // runs past this sub-range (Z): it is the last segment, acc stays as it is
+        hasZ = true;
+        sZ = s;
+        lZ = lsum;
+      }
+      cur_s = -1;
     }
-    cur_s = -1;
   }
+
+  // ---- merge what crosses the sub-ranges of this work-group; hand the rest to the merge kernel
+  __syncthreads();  // every wave is done with its V tile: the region now holds wave states
+  const int sb = sk_state_bytes(D, G);
+  auto st_acc = [&](int w, int slot) { return reinterpret_cast<f32x4*>(s_work + (w * 2 + slot) * sb); };
+  auto st_ml = [&](int w, int slot) { return reinterpret_cast<float2*>(s_work + (w * 2 + slot) * sb + NC * 4 * G * 16); };
+  if (r16 < G) {
+    if (hasA) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) st_acc(wave, 0)[(c * 4 + grp) * G + r16] = accA[c];
+      if (grp == 0) st_ml(wave, 0)[r16] = make_float2(mA, lA);
+    }
+    if (hasZ) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) st_acc(wave, 1)[(c * 4 + grp) * G + r16] = acc[c];
+      if (grp == 0) st_ml(wave, 1)[r16] = make_float2(m_run, lZ);
+    }
+  }
+  if (lane == 0) {
+    s_flags[wave][0] = hasA;
+    s_flags[wave][1] = a_through;
+    s_flags[wave][2] = hasZ;
+    s_flags[wave][3] = sA;
+    s_flags[wave][4] = sZ;
+  }
+  __syncthreads();
+  if (sw != 0 || !head_ok || r16 >= G) return;
+  // Walk the sub-ranges of head column hw in order.  A chain is a sequence cut by sub-range boundaries; it is
+  // finished here when it starts and ends inside the work-group, and otherwise leaves one
+  // record: slot 0 if it began before this work-group's range, slot 1 if it only runs past it.
+  bool open = false, before = false;
+  float cm = kNegBig, cl = 0.f;
+  f32x4 ca[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) ca[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto absorb = [&](int w, int slot) {
+    const float2 ml = st_ml(w, slot)[r16];
+    const float mn = fmaxf(cm, ml.x);
+    const float f0 = __builtin_amdgcn_exp2f(cm - mn), f1 = __builtin_amdgcn_exp2f(ml.x - mn);
+    cl = cl * f0 + ml.y * f1;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) ca[c] = ca[c] * f0 + st_acc(w, slot)[(c * 4 + grp) * G + r16] * f1;
+    cm = mn;
+  };
+  auto restart = [&]() {
+    cm = kNegBig;
+    cl = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) ca[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  auto record = [&](int slot) {
+    const int64_t rec = (static_cast<int64_t>(wgr) * p.num_kv_heads + g) * 2 + slot;
+    float* pa = p.ws_acc + rec * (16 * D) + r16 * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(pa + 16 * c + 4 * grp) = ca[c];
+    if (grp == 0) *reinterpret_cast<float2*>(p.ws_ml + rec * 32 + r16 * 2) = make_float2(cm, cl);
+  };
+  for (int sp = 0; sp < kSplits; ++sp) {
+    const int w = sp * kHeads + hw;
+    if (s_flags[w][0]) {
+      if (!open) {  // no earlier sub-range of this work-group holds it: it began before the range
+        open = true;
+        before = true;
+        restart();
+      }
+      absorb(w, 0);
+      if (!s_flags[w][1]) {  // ends inside sub-range sp
+        if (before) {
+          record(0);
+        } else {
+          const float inv = cl > 0.f ? 1.f / cl : 0.f;
+          raw* o = static_cast<raw*>(p.out) + (static_cast<int64_t>(s_flags[w][3]) * p.num_q_heads + g * G + r16) * D;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) store4<T>(o + 16 * c + 4 * grp, ca[c] * inv);
+        }
+        open = false;
+      }
+    }
+    if (s_flags[w][2]) {
+      open = true;
+      before = false;
+      restart();
+      absorb(w, 1);
+    }
+  }
+  if (open) record(before ? 0 : 1);
 }
 
 // Merge of the sequences cut by range boundaries, and zeros for empty sequences.  One
@@ -416,8 +562,8 @@ __global__ __launch_bounds__(256) void merge_sk_kernel(SkParams p) {
 
 template <typename T, int D>
 hipError_t launch(const SkParams& p, hipStream_t stream) {
-  const int hgroups = (p.num_kv_heads + kWaves - 1) / kWaves;
-  const size_t lds = static_cast<size_t>(p.num_seqs + 1) * sizeof(int);
+  const size_t lds = static_cast<size_t>(sk_lds_bytes(p.num_seqs, D, p.group));
+  const int hgroups = (p.num_kv_heads + kHeads - 1) / kHeads;
   hipLaunchKernelGGL((decode_sk_kernel<T, D>), dim3(p.ranges * hgroups), dim3(kThreads), lds, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -428,15 +574,20 @@ hipError_t launch(const SkParams& p, hipStream_t stream) {
 }  // namespace
 
 int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
-  // About 8 waves per CU on a 256-CU part, and at least 8 tiles per range in the worst case.
+  // About 8 waves per CU on a 256-CU part (4 per work-group, one work-group per range and
+  // KV head), and at least 32 tiles per range (8 per wave) in the worst case.
   const int64_t max_blocks = (static_cast<int64_t>(max_context_len) + kBlock - 1) / kBlock;
   const int64_t upper_tiles = static_cast<int64_t>(num_seqs) * max_blocks;
-  const int32_t hgroups = (num_kv_heads + kWaves - 1) / kWaves;
-  int64_t r = kSkTargetWaves / (static_cast<int64_t>(hgroups) * kWaves);
+  const int64_t hgroups = (num_kv_heads + kHeads - 1) / kHeads;
+  int64_t r = kSkTargetWaves / (hgroups * kWaves);
   if (r < 1) r = 1;
-  const int64_t cap = (upper_tiles + 7) / 8;
+  const int64_t cap = (upper_tiles + 31) / 32;
   if (r > cap) r = cap;
   return static_cast<int32_t>(r < 1 ? 1 : r);
+}
+
+int sk_lds_bytes_host(int32_t num_seqs, int32_t head_dim, int32_t group) {
+  return sk_lds_bytes(num_seqs, head_dim, group);
 }
 
 size_t sk_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len) {

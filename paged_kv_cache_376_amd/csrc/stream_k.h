@@ -17,12 +17,14 @@ constexpr int kSkMaxSeqs = 8192;
 struct SkParams {
   void* out;
   const void* q;
-  const void* k_cache;
-  const void* v_cache;
+  void* k_cache;  // written only with a fused append (new_key != NULL)
+  void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_acc;   // [ranges][Hkv][2][16][D]  unnormalised acc of cut sequences
-  float* ws_ml;    // [ranges][Hkv][2][16][2]  (running max, sum)
+  const void* new_key;    // [B][Hkv][D] or NULL: with a fused append, each sequence's new
+  const void* new_value;  // token (its last one) comes from here and is written to its slot
+  float* ws_acc;   // [ranges][Hkv][2][16][D]  unnormalised acc of sequences cut by ranges
+  float* ws_ml;    // [ranges][Hkv][2][16][2]  (running max, sum); ranges are per work-group
   int32_t* ws_cu;  // [B + 1] prefix sum of block counts, written by the decode kernel
   int32_t num_seqs;
   int32_t num_q_heads;
@@ -32,12 +34,14 @@ struct SkParams {
   int32_t max_blocks_per_seq;
   int32_t max_context_len;
   int32_t num_blocks;
-  int32_t ranges;  // equal tile ranges per KV head
+  int32_t ranges;  // equal tile ranges per KV head (one work-group of 4 waves each)
   float scale_log2e;
 };
 
 // Ranges per KV head for these arguments (host).
 int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len);
+// LDS bytes of the decode kernel for these shapes (host); above 64 KiB needs no opt-in here.
+int sk_lds_bytes_host(int32_t num_seqs, int32_t head_dim, int32_t group);
 // Workspace bytes the path needs (host).
 size_t sk_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len);
 // Enqueues the decode kernel and the merge kernel on `stream`.

@@ -30,6 +30,27 @@ def decode_step(w, partition_size=0, fill=float("nan"), q=None):
     return out, cache, bt, ctx, maxc
 
 
+def decode_step_fused(w, partition_size=0, fill=float("nan")):
+    """Build the pool, let the host pool take each sequence's next slot (copy-on-write copies
+    done), then one pkv_paged_attn_decode_append call.  Returns (out_cpu, cache, bt, ctx, maxc,
+    slots)."""
+    cache = build_cache(w, DEVICE, fill=fill)
+    seqs = list(range(w.spec.num_seqs))
+    slots = np.zeros(len(seqs), dtype=np.int64)
+    for i, s in enumerate(seqs):
+        sl, cow = cache.pool.seq_extend(s, 1)
+        cache.copy_blocks(cow)
+        slots[i] = sl[0]
+    bt, ctx, maxc = cache.tables(seqs)
+    qd = w.q.to(DEVICE).contiguous()
+    out = torch.empty_like(qd)
+    binding.paged_attn_decode_append(out, qd, w.new_k.to(DEVICE).contiguous(), w.new_v.to(DEVICE).contiguous(),
+                                     cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale,
+                                     partition_size=partition_size)
+    torch.cuda.synchronize()
+    return out.cpu(), cache, bt, ctx, maxc, slots
+
+
 def decode(cache, q, bt, ctx, maxc, scale, partition_size=0):
     qd = q.to(DEVICE).contiguous()
     out = torch.empty_like(qd)

@@ -7,7 +7,7 @@ import torch
 import oracle
 from paged_kv_cache_376_amd import binding, workloads as W
 from paged_kv_cache_376_amd.cache import build_cache
-from tests.gpu_common import DEVICE, bits, say
+from tests.gpu_common import DEVICE, TOL, bits, decode_step, decode_step_fused, max_err, oracle_out, say
 
 pytestmark = pytest.mark.gpu
 
@@ -81,3 +81,48 @@ def test_decode_step_append_full_size(name):
         assert ctx[s] == k.shape[0]
         assert np.array_equal(oracle.gather_sequence(kc, bt[s], ctx[s]), bits(k).numpy())
         assert np.array_equal(oracle.gather_sequence(vc, bt[s], ctx[s]), bits(v).numpy())
+
+
+FUSED = [
+    # (spec overrides, partition): even split (G > 2), fixed partitions, MHA, fp32
+    (W.SPECS["gqa_bf16"].replace(num_seqs=10, len_hi=900), 0),
+    (W.SPECS["gqa_bf16"].replace(num_seqs=10, len_hi=900), 64),
+    (W.Spec("f16g4d64", "float16", 6, 16, 4, 64, "fixed", fixed_lengths=(15, 16, 31, 200, 1, 600)), 0),
+    (W.SPECS["mha_fp16"].replace(num_seqs=5, len_lo=100, len_hi=400), 0),
+    (W.SPECS["tiny_fp32"], 0),
+    # prefix groups whose shared prefix ends inside a block: copy-on-write before the append
+    (W.SPECS["prefix_bf16"].replace(num_seqs=16, prefix_len=40, suffix_hi=30), 0),
+]
+
+
+@pytest.mark.parametrize("spec,partition", FUSED, ids=[f"{sp.name}-p{pt}" for sp, pt in FUSED])
+def test_fused_decode_append(spec, partition):
+    """pkv_paged_attn_decode_append: pools equal the oracle scatter bit for bit, the output
+    equals the separate append + decode calls bit for bit, and matches the fp64 oracle."""
+    say(f"[fused] {spec.name} partition={partition}")
+    w = W.Workload(spec, seed=3)
+    cache0 = __import__("paged_kv_cache_376_amd.cache", fromlist=["build_cache"]).build_cache(w, DEVICE, fill=float("nan"))
+    kc0, vc0 = bits(cache0.k_cache.cpu()).numpy(), bits(cache0.v_cache.cpu()).numpy()
+    del cache0
+    out, cache, bt, ctx, maxc, slots = decode_step_fused(w, partition_size=partition)
+    ref_sep, *_ = decode_step(w, partition_size=partition)
+    assert torch.equal(bits(out), bits(ref_sep))
+    err = max_err(out, oracle_out(w))
+    say(f"    max abs err {err:.3e}")
+    assert err <= TOL[spec.dtype], err
+    # pools: the oracle scatter of the new rows (copy-on-write copies happened before)
+    kc, vc = bits(cache.k_cache.cpu()).numpy(), bits(cache.v_cache.cpu()).numpy()
+    bt_h, ctx_h = bt.cpu().numpy(), ctx.cpu().numpy()
+    for s in range(spec.num_seqs):
+        k, v = w.seq_kv_after_append(s)
+        assert ctx_h[s] == k.shape[0]
+        assert np.array_equal(oracle.gather_sequence(kc, bt_h[s], ctx_h[s]), bits(k).numpy())
+        assert np.array_equal(oracle.gather_sequence(vc, bt_h[s], ctx_h[s]), bits(v).numpy())
+    # nothing but the new slots (and copy-on-write destinations) changed
+    changed = np.nonzero((kc != kc0).reshape(kc.shape[0] * kc.shape[1], -1).any(axis=1))[0]
+    cow_dst = set()
+    for s in range(spec.num_seqs):
+        for b in bt_h[s][: -(-int(ctx_h[s]) // 16)]:
+            cow_dst.add(int(b))
+    assert set((changed // 16).tolist()) <= cow_dst
+    assert set(slots.tolist()) <= set(changed.tolist())
