@@ -48,6 +48,26 @@ def algorithmic_bytes(w):
     return kv, kv + qo + tables
 
 
+COUNTERS = os.path.join(ROOT, "profiles", "decode_gqa_bf16_B256_counters.md")
+SK_SOURCE = os.path.join(ROOT, "paged_kv_cache_376_amd", "csrc", "paged_attn_sk.hip")
+
+
+def counter_traffic():
+    """Calibrated HBM bytes of one decode call from the committed rocprofv3 counter summary,
+    or None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+
+    try:
+        text = open(COUNTERS, encoding="utf-8").read()
+        want = re.search(r"kernel_source_sha256: ([0-9a-f]{64})", text).group(1)
+        value = int(re.search(r"traffic_bytes_per_call: (\d+)", text).group(1))
+        have = hashlib.sha256(open(SK_SOURCE, "rb").read()).hexdigest()
+    except (OSError, AttributeError):
+        return None
+    return value if have == want else None
+
+
 def cpu_baseline(w, budget_s=15.0):
     """The fp64 oracle on the host cores over a bounded sample of the same workload."""
     import numpy as np
@@ -257,7 +277,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            # counters were taken on the default workload with the fused call
+            "traffic": counter_traffic() if (args.config == "gqa_bf16" and args.seed == 0 and not args.separate
+                                             and args.partition == 0) else None,
             "bytes_per_launch": dec_bytes,
             "avg_launch_us": round(dec_s * 1e6, 2),
         },
