@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from paged_kv_cache_376_amd import workloads as W
-from tests.gpu_common import TOL, decode_step, max_err, oracle_out, say
+from tests.gpu_common import TOL, decode_step, decode_step_fused, max_err, oracle_out, say
 
 pytestmark = pytest.mark.gpu
 
@@ -95,3 +95,22 @@ def test_shapes_match_oracle(dtype, hq, hkv, d, lens, partition):
     err = max_err(out, oracle_out(w))
     say(f"    max abs err {err:.3e}")
     assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("name", ["gqa_bf16", "long_bf16", "prefix_bf16", "mha_fp16"])
+def test_full_size_fused_sampled(name):
+    """The benchmark's own call (pkv_paged_attn_decode_append, default work split) at full
+    size: every output finite, sampled sequences (longest, shortest, 6 random) against the
+    oracle."""
+    say(f"[parity full fused] {name}")
+    w = W.make_workload(name, 0)
+    out, *_ = decode_step_fused(w)
+    assert torch.isfinite(out.float()).all()
+    lens = w.context_lens
+    rng = np.random.default_rng(17)
+    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
+    pick |= set(rng.choice(w.spec.num_seqs, size=min(6, w.spec.num_seqs), replace=False).tolist())
+    seqs = sorted(pick)
+    err = max_err(out[seqs], oracle_out(w, seqs))
+    say(f"    sampled seqs {seqs}: max abs err {err:.3e}")
+    assert err <= TOL[w.spec.dtype], err
