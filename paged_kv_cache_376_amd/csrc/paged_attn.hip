@@ -654,7 +654,7 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
     const int64_t recs = static_cast<int64_t>(sp.ranges) * sp.num_kv_heads * 2;
     sp.ws_acc = static_cast<float*>(workspace);
     sp.ws_ml = sp.ws_acc + recs * 16 * D;
-    sp.ws_cu = reinterpret_cast<int32_t*>(sp.ws_ml + recs * 32);
+    sp.ws_desc = reinterpret_cast<int32_t*>(sp.ws_ml + recs * 32);
     const hipError_t err = sk::sk_launch(sp, cache->dtype, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
     return PKV_OK;

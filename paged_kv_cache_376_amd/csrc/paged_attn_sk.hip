@@ -11,16 +11,18 @@
 //
 // Work split.  A "tile" is one 16-token block of one sequence for one KV head (K and V:
 // 2*16*D*e bytes).  For one KV head the tiles of all sequences form a list in sequence order
-// (block 0..nblk-1 of sequence 0, then sequence 1, ...), T tiles long.  The list is cut into
-// `ranges` equal contiguous ranges.  A work-group of 4 waves serves one range for 4
-// consecutive KV heads, one head per wave, so the waves of a work-group read neighbouring
-// 256-byte slices of the same token rows at the same time.  Every wave therefore streams
-// the same number of tiles (+-1) whatever the length mix, and keeps loading across sequence
-// boundaries.
-//   * A sequence whose tiles lie inside one range is finished by that wave (output written).
+// (block 0..nblk-1 of sequence 0, then sequence 1, ...), T tiles long; a sequence with no
+// context counts as one empty tile, so that its zero output is written like any other.  The
+// list is cut into R equal contiguous ranges (R never exceeds T, so no range is empty).  A
+// work-group serves one range for 4 consecutive KV heads, one head per wave column, so its
+// waves read neighbouring 256-byte slices of the same token rows at the same time; the range
+// is split again between 2 wave rows.  Every wave therefore streams the same number of tiles
+// (+-1) whatever the length mix, and keeps loading across sequence boundaries.
+//   * A sequence whose tiles lie inside one wave's sub-range is finished by that wave.
+//   * A sequence cut only between the two sub-ranges of a work-group is merged in LDS.
 //   * A sequence cut by range boundaries leaves one record (unnormalised acc, running max m,
-//     sum l) per wave that touched it; the merge kernel combines them in wave order.
-// Each work-group derives its range from the context lengths itself (prefix sum of block
+//     sum l) per work-group that touched it; the merge kernel combines them in range order.
+// Each work-group derives its range from the context lengths itself (prefix sum of tile
 // counts in LDS), so no planning launch is needed.
 //
 // Per tile (one wave, 16 tokens, G <= 16 query heads padded to 16):
@@ -120,6 +122,34 @@ __device__ __forceinline__ void store4(typename T::raw* dst, f32x4 v) {
   *reinterpret_cast<uint2*>(dst) = w;
 }
 
+// Writes a wave's G output rows, which are contiguous in memory (row r16 < G holds columns
+// 16c + 4grp .. +3 in v[c]), as 16-byte stores of consecutive lanes.  The rows are staged in
+// `stage`, this wave's own LDS (at least G * (2D + 16) bytes), with a padded row pitch.
+template <typename T, int D>
+__device__ __forceinline__ void store_rows(typename T::raw* o, const f32x4* v, float inv, unsigned char* stage,
+                                           int G, int lane) {
+  constexpr int SP = 2 * D + 16;
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  const int r16 = lane & 15, grp = lane >> 4;
+  if (r16 < G) {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const f32x4 x = v[c] * inv;
+      uint2 w;
+      w.x = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_raw(T{}, x[0]))) |
+            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_raw(T{}, x[1]))) << 16);
+      w.y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_raw(T{}, x[2]))) |
+            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_raw(T{}, x[3]))) << 16);
+      *reinterpret_cast<uint2*>(stage + r16 * SP + 32 * c + 8 * grp) = w;
+    }
+  }
+  wave_lds_sync();
+  for (int q = lane; q < G * CPR; q += 64)
+    *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(o) + 16 * q) =
+        *reinterpret_cast<const u32x4*>(stage + (q / CPR) * SP + 16 * (q % CPR));
+  wave_lds_sync();
+}
+
 // Per-lane tile entry of tile t (t < T): {physical block, sequence, block index, ntok | kLast}.
 __device__ __forceinline__ int4 tile_entry(const SkParams& p, const int* s_cu, int t) {
   int a = 0, b = p.num_seqs;  // largest a with cu[a] <= t  (cu[0] = 0 <= t < cu[B] = T)
@@ -130,7 +160,8 @@ __device__ __forceinline__ int4 tile_entry(const SkParams& p, const int* s_cu, i
   const int j = t - s_cu[a];
   const int nblk = s_cu[a + 1] - s_cu[a];
   const int L = clamp_ctx(p.context_lens[a], p.max_context_len);
-  const int phys = p.block_tables[static_cast<int64_t>(a) * p.max_blocks_per_seq + j];
+  // the empty tile of a sequence with no context reads nothing (block id -1) and has 0 tokens
+  const int phys = L > 0 ? p.block_tables[static_cast<int64_t>(a) * p.max_blocks_per_seq + j] : -1;
   const int ntok = min(kBlock, L - j * kBlock);
   return make_int4(phys, a, j, ntok | (j == nblk - 1 ? kLast : 0));
 }
@@ -174,36 +205,53 @@ void decode_sk_kernel(SkParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
   int* s_cu = reinterpret_cast<int*>(s_dyn);                  // [B + 1]
   unsigned char* s_work = s_dyn + sk_cu_bytes(B);              // V tiles, later wave states
-  __shared__ int s_part[kThreads];
+  __shared__ int s_part[kWaves];
   __shared__ int s_flags[kWaves][5];
 
-  // ---- prefix sum of block counts (every work-group derives the same list)
+  // ---- prefix sum of tile counts (every work-group derives the same list)
   const int per = (B + kThreads - 1) / kThreads;
   const int lo = min(B, tid * per), hi = min(B, lo + per);
   int run = 0;
   for (int s = lo; s < hi; ++s) {
-    run += (clamp_ctx(p.context_lens[s], p.max_context_len) + kBlock - 1) / kBlock;
+    run += max(1, (clamp_ctx(p.context_lens[s], p.max_context_len) + kBlock - 1) / kBlock);
     s_cu[s + 1] = run;
   }
-  s_part[tid] = run;
-  __syncthreads();
-  for (int o = 1; o < kThreads; o <<= 1) {
-    const int v = tid >= o ? s_part[tid - o] : 0;
-    __syncthreads();
-    s_part[tid] += v;
-    __syncthreads();
+  // exclusive offset of this thread's sequences: a scan within the wave, then over the waves
+  int incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
   }
-  const int base = tid > 0 ? s_part[tid - 1] : 0;
+  if (lane == 63) s_part[wave] = incl;
+  __syncthreads();
+  int base = incl - run;
+  for (int w = 0; w < wave; ++w) base += s_part[w];
   for (int s = lo; s < hi; ++s) s_cu[s + 1] += base;
   if (tid == 0) s_cu[0] = 0;
   __syncthreads();
   const int ntiles = s_cu[B];
-  if (blockIdx.x == 0) {  // the merge kernel reads the prefix sum from here
-    for (int s = tid; s <= B; s += kThreads) p.ws_cu[s] = s_cu[s];
+  const int R = min(p.ranges, ntiles);  // ranges in use: none of them is empty
+  if (hg == 0 && tid == 0) {
+    // the merge kernel's work list: the sequence cut at this range's start, if this is the
+    // first range boundary inside it, with the ranges that hold its first and last tiles
+    int4 d = make_int4(-1, 0, 0, 0);
+    if (wgr > 0 && wgr < R) {
+      const int T0 = static_cast<int>(static_cast<int64_t>(wgr) * ntiles / R);
+      int a = 0, b = B;  // largest a with s_cu[a] <= T0
+      while (b - a > 1) {
+        const int m = (a + b) >> 1;
+        if (s_cu[m] <= T0) a = m; else b = m;
+      }
+      const int ra = range_of(s_cu[a], ntiles, R);
+      if (s_cu[a] < T0 && ra == wgr - 1) d = make_int4(a, ra, range_of(s_cu[a + 1] - 1, ntiles, R), 0);
+    }
+    *reinterpret_cast<int4*>(p.ws_desc + 4 * wgr) = d;
   }
+  if (wgr >= R) return;  // more work-groups than tiles
   // this work-group's range of the head's tile list, and this wave's sub-range of it
-  const int T0 = static_cast<int>(static_cast<int64_t>(wgr) * ntiles / p.ranges);
-  const int T1 = static_cast<int>(static_cast<int64_t>(wgr + 1) * ntiles / p.ranges);
+  const int T0 = static_cast<int>(static_cast<int64_t>(wgr) * ntiles / R);
+  const int T1 = static_cast<int>(static_cast<int64_t>(wgr + 1) * ntiles / R);
   const int t0 = T0 + static_cast<int>(static_cast<int64_t>(T1 - T0) * sw / kSplits);
   const int t1 = T0 + static_cast<int>(static_cast<int64_t>(T1 - T0) * (sw + 1) / kSplits);
   const int n = head_ok ? t1 - t0 : 0;
@@ -297,20 +345,12 @@ void decode_sk_kernel(SkParams p) {
       }
       if (append && (fl & kLast)) {
         // the sequence's new token is its last one (row ntok - 1 of this block): use the new
-        // row and write it to its pool slot
+        // row (the merge kernel writes it to its pool slot)
         const bool mine = r16 == ntok - 1;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
           kbuf[c] = mine ? nk[c] : kbuf[c];
           vbuf[c] = mine ? nv[c] : vbuf[c];
-        }
-        const int phys = lane_val(ent.x, i);
-        if (mine && phys >= 0 && phys < p.num_blocks) {
-#pragma unroll
-          for (int c = 0; c < KC; ++c) {
-            *reinterpret_cast<u32x4*>(kbase + phys * block_bytes + voff + c * 64) = kbuf[c];
-            *reinterpret_cast<u32x4*>(vbase + phys * block_bytes + voff + c * 64) = vbuf[c];
-          }
         }
       }
       // V tile -> LDS (row = token r16), then S^T = K Q^T
@@ -372,12 +412,9 @@ void decode_sk_kernel(SkParams p) {
       if (!seg_end) continue;
       const float lsum = swap32_sum(swap16_sum(l_run));
       if (seg_j0 == 0 && (fl & kLast)) {  // the whole sequence lies in this wave's sub-range
-        if (r16 < G) {
-          const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-          raw* o = static_cast<raw*>(p.out) + (static_cast<int64_t>(s) * p.num_q_heads + g * G + r16) * D;
-#pragma unroll
-          for (int c = 0; c < NC; ++c) store4<T>(o + 16 * c + 4 * grp, acc[c] * inv);
-        }
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        store_rows<T, D>(static_cast<raw*>(p.out) + (static_cast<int64_t>(s) * p.num_q_heads + g * G) * D, acc, inv,
+                         vt, G, lane);
       } else if (seg_k0 == 0 && seg_j0 > 0) {  // began in an earlier sub-range (A)
         hasA = true;
         a_through = !(fl & kLast);
@@ -482,81 +519,138 @@ void decode_sk_kernel(SkParams p) {
   if (open) record(before ? 0 : 1);
 }
 
-// Merge of the sequences cut by range boundaries, and zeros for empty sequences.  One
-// work-group of 4 waves per (KV head, sequence): wave v folds in records v, v + 4, ... of the
-// ranges that touched the sequence (two at a time, loads in flight together), then wave 0
-// combines the 4 partial results in a fixed order.  Deterministic.
+// Merge of the sequences cut by range boundaries, and the pool writes of a fused append.
+//
+// One work-group of 8 waves per (range r, group of 4 KV heads).  The range's descriptor names
+// the sequence whose first cut lies at the range's start (or none).  Such a sequence has its
+// first tile in range r - 1 and spans ranges r - 1 .. rb, so its first two records (range
+// r - 1, slot 1; range r, slot 0) are loaded before the descriptor arrives.  Two waves serve
+// each KV head of the group: after that first pair (wave row 0), the records of ranges
+// r + 1 + 4k .. r + 4 + 4k go to wave row k % 2, four loads in flight; wave row 0 then adds row
+// 1's result and writes the output.  The order is fixed: deterministic.
+//
+// With a fused append the decode kernel took each sequence's new K/V row from new_key /
+// new_value; wave row 1 of this kernel writes those rows to their pool slots (position
+// context_len - 1, found through the block table), work-group r taking sequences r,
+// r + ranges, ...  Wave row 0 waits for row 1's partial result on an LDS flag rather than a
+// work-group barrier, so the append does not hold up the merge.
+constexpr int kMergeThreads = 512;
+__host__ __device__ inline int merge_lds_bytes(int D) { return kHeads * ((D / 16) * 64 * 16 + 64 * 8); }
+
+// Folds U records (loaded into x / ml; u valid when u < nvalid) into the running (m, l, a).
+template <int U, int NC>
+__device__ __forceinline__ void fold_records(float& m, float& l, f32x4* a, const float2* ml, f32x4 (*x)[NC], int nvalid) {
+  float mn = m;
+#pragma unroll
+  for (int u = 0; u < U; ++u) mn = u < nvalid ? fmaxf(mn, ml[u].x) : mn;
+  const float f0 = __builtin_amdgcn_exp2f(m - mn);
+  l *= f0;
+#pragma unroll
+  for (int q = 0; q < NC; ++q) a[q] *= f0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float f = u < nvalid ? __builtin_amdgcn_exp2f(ml[u].x - mn) : 0.f;
+    l = fmaf(ml[u].y, f, l);
+#pragma unroll
+    for (int q = 0; q < NC; ++q) a[q] += x[u][q] * f;
+  }
+  m = mn;
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void merge_sk_kernel(SkParams p) {
+__global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
   using raw = typename T::raw;
   constexpr int NC = D / 16;
-  const int g = blockIdx.x, s = blockIdx.y;
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  constexpr int U = 4;  // records in flight per wave after the first pair
+  const int hgroups = (p.num_kv_heads + kHeads - 1) / kHeads;
+  const int r = blockIdx.x / hgroups, hg = blockIdx.x % hgroups;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int hw = wave % kHeads, pw = wave / kHeads;
+  const int g = hg * kHeads + hw;
+  const bool live = g < p.num_kv_heads;
   const int G = p.group;
-  const int ntiles = p.ws_cu[p.num_seqs];
-  const int c0 = p.ws_cu[s], nblk = p.ws_cu[s + 1] - c0;
-  raw* o = static_cast<raw*>(p.out) + (static_cast<int64_t>(s) * p.num_q_heads + g * G + (r16 < G ? r16 : 0)) * D;
-  if (nblk == 0) {  // empty context: zeros
-    if (wv == 0 && r16 < G) {
+  const int hr = r16 < G ? r16 : 0;  // rows past the group repeat row 0 (never stored)
+  auto rec_of = [&](int c, int slot) { return (static_cast<int64_t>(c) * p.num_kv_heads + g) * 2 + slot; };
+  auto load_rec = [&](int64_t rec, float2& ml, f32x4* x) {
+    ml = *reinterpret_cast<const float2*>(p.ws_ml + rec * 32 + hr * 2);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) store4<T>(o + 16 * c + 4 * grp, f32x4{0.f, 0.f, 0.f, 0.f});
-    }
-    return;
+    for (int q = 0; q < NC; ++q) x[q] = *reinterpret_cast<const f32x4*>(p.ws_acc + rec * (16 * D) + hr * D + 16 * q + 4 * grp);
+  };
+  extern __shared__ __attribute__((aligned(16))) unsigned char s_merge[];
+  f32x4* s_a = reinterpret_cast<f32x4*>(s_merge + hw * (NC * 64 * 16 + 64 * 8));
+  float2* s_ml = reinterpret_cast<float2*>(s_merge + hw * (NC * 64 * 16 + 64 * 8) + NC * 64 * 16);
+  __shared__ int s_ready[kHeads];  // wave row 1 has left its partial result for head column hw
+
+  const int4 d = *reinterpret_cast<const int4*>(p.ws_desc + 4 * r);
+  float2 ml0[2];
+  f32x4 x0[2][NC];
+  const bool first = pw == 0 && live && r > 0;
+  if (first) {
+    load_rec(rec_of(r - 1, 1), ml0[0], x0[0]);
+    load_rec(rec_of(r, 0), ml0[1], x0[1]);
   }
-  const int ra = range_of(c0, ntiles, p.ranges), rb = range_of(c0 + nblk - 1, ntiles, p.ranges);
-  if (ra == rb) return;  // finished by its range
-  const int nc = rb - ra + 1;
-  const int hr = r16 < G ? r16 : 0;
-  float m = kNegBig, l = 0.f;
-  f32x4 a[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) a[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int c = wv; c < nc; c += 8) {
-    const bool two = c + 4 < nc;
-    const int64_t r1 = (static_cast<int64_t>(ra + c) * p.num_kv_heads + g) * 2 + (c == 0 ? 1 : 0);
-    const int64_t r2 = two ? (static_cast<int64_t>(ra + c + 4) * p.num_kv_heads + g) * 2 : r1;
-    const float m1 = p.ws_ml[r1 * 32 + r16 * 2], l1 = p.ws_ml[r1 * 32 + r16 * 2 + 1];
-    const float m2 = two ? p.ws_ml[r2 * 32 + r16 * 2] : kNegBig;
-    const float l2 = two ? p.ws_ml[r2 * 32 + r16 * 2 + 1] : 0.f;
-    f32x4 x1[NC], x2[NC];
-#pragma unroll
-    for (int q = 0; q < NC; ++q) x1[q] = *reinterpret_cast<const f32x4*>(p.ws_acc + r1 * (16 * D) + hr * D + 16 * q + 4 * grp);
-#pragma unroll
-    for (int q = 0; q < NC; ++q) x2[q] = *reinterpret_cast<const f32x4*>(p.ws_acc + r2 * (16 * D) + hr * D + 16 * q + 4 * grp);
-    const float mn = fmaxf(m, fmaxf(m1, m2));
-    const float f0 = __builtin_amdgcn_exp2f(m - mn), f1 = __builtin_amdgcn_exp2f(m1 - mn);
-    const float f2 = two ? __builtin_amdgcn_exp2f(m2 - mn) : 0.f;
-    l = l * f0 + l1 * f1 + l2 * f2;
-#pragma unroll
-    for (int q = 0; q < NC; ++q) a[q] = a[q] * f0 + x1[q] * f1 + x2[q] * f2;
-    m = mn;
-  }
-  __shared__ f32x4 s_a[4][NC][64];
-  __shared__ float s_m[4][64], s_l[4][64];
-#pragma unroll
-  for (int q = 0; q < NC; ++q) s_a[wv][q][lane] = a[q];
-  s_m[wv][lane] = m;
-  s_l[wv][lane] = l;
+  if (tid < kHeads) s_ready[tid] = 0;
   __syncthreads();
-  if (wv != 0) return;
-  float Mx = s_m[0][lane];
+
+  if (d.x >= 0) {  // uniform over the work-group
+    const int s = d.x, rb = d.z;  // d.y == r - 1
+    float m = kNegBig, l = 0.f;
+    f32x4 a[NC];
 #pragma unroll
-  for (int v = 1; v < 4; ++v) Mx = fmaxf(Mx, s_m[v][lane]);
-  float L = 0.f;
-  f32x4 r[NC];
+    for (int q = 0; q < NC; ++q) a[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (first) fold_records<2, NC>(m, l, a, ml0, x0, 2);
+    for (int c0 = r + 1 + U * pw; live && c0 <= rb; c0 += 2 * U) {
+      float2 ml[U];
+      f32x4 x[U][NC];
 #pragma unroll
-  for (int q = 0; q < NC; ++q) r[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < U; ++u) load_rec(rec_of(c0 + u <= rb ? c0 + u : c0, 0), ml[u], x[u]);
+      __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the first use
+      fold_records<U, NC>(m, l, a, ml, x, rb - c0 + 1);
+    }
+    if (pw == 1) {  // hand the partial result to wave row 0 (no work-group barrier: row 1 goes on)
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const float f = __builtin_amdgcn_exp2f(s_m[v][lane] - Mx);
-    L = fmaf(s_l[v][lane], f, L);
+      for (int q = 0; q < NC; ++q) s_a[q * 64 + lane] = a[q];
+      s_ml[lane] = make_float2(m, l);
+      __hip_atomic_store(&s_ready[hw], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+      // row 1 of the same work-group always sets the flag; the cap only bounds the wait
+      for (int spin = 0; spin < (1 << 22) &&
+                         __hip_atomic_load(&s_ready[hw], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
+           ++spin)
+        __builtin_amdgcn_s_sleep(1);
+      if (live && r16 < G) {
+        const float2 o1 = s_ml[lane];
+        const float mn = fmaxf(m, o1.x);
+        const float f0 = __builtin_amdgcn_exp2f(m - mn), f1 = __builtin_amdgcn_exp2f(o1.x - mn);
+        const float L = l * f0 + o1.y * f1;
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        raw* o = static_cast<raw*>(p.out) + (static_cast<int64_t>(s) * p.num_q_heads + g * G + r16) * D;
 #pragma unroll
-    for (int q = 0; q < NC; ++q) r[q] += s_a[v][q][lane] * f;
+        for (int q = 0; q < NC; ++q) store4<T>(o + 16 * q + 4 * grp, (a[q] * f0 + s_a[q * 64 + lane] * f1) * inv);
+      }
+    }
   }
-  if (r16 < G) {
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-    for (int q = 0; q < NC; ++q) store4<T>(o + 16 * q + 4 * grp, r[q] * inv);
+
+  if (p.new_key != nullptr && pw == 1) {  // fused append (wave row 1): new rows to their slots
+    constexpr int CPR = D * static_cast<int>(sizeof(raw)) / 16;  // 16-byte chunks per row
+    constexpr int kRowThreads = kMergeThreads / 2;
+    const int64_t row_bytes = static_cast<int64_t>(D) * sizeof(raw);
+    const int t = tid - kRowThreads, ch = 16 * (t % CPR);
+    const int nseq = (p.num_seqs - r + p.ranges - 1) / p.ranges;
+    for (int pi = t / CPR; pi < nseq * kHeads; pi += kRowThreads / CPR) {
+      const int s = r + p.ranges * (pi / kHeads), gg = hg * kHeads + pi % kHeads;
+      if (gg >= p.num_kv_heads) continue;
+      const int L = clamp_ctx(p.context_lens[s], p.max_context_len);
+      if (L == 0) continue;
+      const int phys = p.block_tables[static_cast<int64_t>(s) * p.max_blocks_per_seq + (L - 1) / kBlock];
+      if (phys < 0 || phys >= p.num_blocks) continue;
+      const int64_t src = (static_cast<int64_t>(s) * p.num_kv_heads + gg) * row_bytes + ch;
+      const int64_t dst = ((static_cast<int64_t>(phys) * kBlock + (L - 1) % kBlock) * p.num_kv_heads + gg) * row_bytes + ch;
+      const u32x4 kr = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(p.new_key) + src);
+      const u32x4 vr = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(p.new_value) + src);
+      *reinterpret_cast<u32x4*>(static_cast<unsigned char*>(p.k_cache) + dst) = kr;
+      *reinterpret_cast<u32x4*>(static_cast<unsigned char*>(p.v_cache) + dst) = vr;
+    }
   }
 }
 
@@ -567,15 +661,16 @@ hipError_t launch(const SkParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_sk_kernel<T, D>), dim3(p.ranges * hgroups), dim3(kThreads), lds, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((merge_sk_kernel<T, D>), dim3(p.num_kv_heads, p.num_seqs), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((merge_sk_kernel<T, D>), dim3(p.ranges * hgroups), dim3(kMergeThreads),
+                     static_cast<size_t>(merge_lds_bytes(D)), stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
-  // About 8 waves per CU on a 256-CU part (4 per work-group, one work-group per range and
-  // KV head), and at least 32 tiles per range (8 per wave) in the worst case.
+  // About 8 waves per CU on a 256-CU part (one work-group of 8 waves per range and group of 4
+  // KV heads), and at least 32 tiles per range in the worst case.
   const int64_t max_blocks = (static_cast<int64_t>(max_context_len) + kBlock - 1) / kBlock;
   const int64_t upper_tiles = static_cast<int64_t>(num_seqs) * max_blocks;
   const int64_t hgroups = (num_kv_heads + kHeads - 1) / kHeads;
@@ -595,8 +690,8 @@ size_t sk_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_d
   const int64_t recs = R * num_kv_heads * 2;
   const size_t acc = static_cast<size_t>(recs) * 16 * head_dim * sizeof(float);
   const size_t ml = static_cast<size_t>(recs) * 32 * sizeof(float);
-  const size_t cu = ((static_cast<size_t>(num_seqs) + 1) * sizeof(int) + 255) / 256 * 256;
-  return acc + ml + cu;
+  const size_t desc = static_cast<size_t>(R) * 4 * sizeof(int32_t);
+  return acc + ml + desc;
 }
 
 hipError_t sk_launch(SkParams p, int32_t dtype, hipStream_t stream) {

@@ -23,9 +23,10 @@ struct SkParams {
   const int32_t* context_lens;
   const void* new_key;    // [B][Hkv][D] or NULL: with a fused append, each sequence's new
   const void* new_value;  // token (its last one) comes from here and is written to its slot
-  float* ws_acc;   // [ranges][Hkv][2][16][D]  unnormalised acc of sequences cut by ranges
-  float* ws_ml;    // [ranges][Hkv][2][16][2]  (running max, sum); ranges are per work-group
-  int32_t* ws_cu;  // [B + 1] prefix sum of block counts, written by the decode kernel
+  float* ws_acc;     // [ranges][Hkv][2][16][D]  unnormalised acc of sequences cut by ranges
+  float* ws_ml;      // [ranges][Hkv][2][16][2]  (running max, sum); ranges are per work-group
+  int32_t* ws_desc;  // [ranges][4] per range: the sequence cut at its start whose merge it owns
+                     // (or -1), with the first and last range holding tiles of that sequence
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
