@@ -111,7 +111,9 @@ __device__ __forceinline__ int range_of(int t, int n, int R) {
   return static_cast<int>(((static_cast<int64_t>(t) + 1) * R - 1) / n);
 }
 
-// Stores 4 fp32 values rounded to the element type as one 8-byte (or 16-byte for fp32) write.
+// Stores 4 fp32 values rounded to the element type as one 8-byte write.  Results and records
+// are written with the non-temporal hint (they are not read again by this launch's waves), which
+// keeps them from displacing K/V lines in L2.
 template <typename T>
 __device__ __forceinline__ void store4(typename T::raw* dst, f32x4 v) {
   uint2 w;
@@ -119,7 +121,8 @@ __device__ __forceinline__ void store4(typename T::raw* dst, f32x4 v) {
         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_raw(T{}, v[1]))) << 16);
   w.y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_raw(T{}, v[2]))) |
         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_raw(T{}, v[3]))) << 16);
-  *reinterpret_cast<uint2*>(dst) = w;
+  __builtin_nontemporal_store(static_cast<unsigned long long>(w.x) | (static_cast<unsigned long long>(w.y) << 32),
+                              reinterpret_cast<unsigned long long*>(dst));
 }
 
 // Writes a wave's G output rows, which are contiguous in memory (row r16 < G holds columns
@@ -145,8 +148,8 @@ __device__ __forceinline__ void store_rows(typename T::raw* o, const f32x4* v, f
   }
   wave_lds_sync();
   for (int q = lane; q < G * CPR; q += 64)
-    *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(o) + 16 * q) =
-        *reinterpret_cast<const u32x4*>(stage + (q / CPR) * SP + 16 * (q % CPR));
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stage + (q / CPR) * SP + 16 * (q % CPR)),
+                                reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(o) + 16 * q));
   wave_lds_sync();
 }
 
@@ -160,8 +163,11 @@ __device__ __forceinline__ int4 tile_entry(const SkParams& p, const int* s_cu, i
   const int j = t - s_cu[a];
   const int nblk = s_cu[a + 1] - s_cu[a];
   const int L = clamp_ctx(p.context_lens[a], p.max_context_len);
-  // the empty tile of a sequence with no context reads nothing (block id -1) and has 0 tokens
-  const int phys = L > 0 ? p.block_tables[static_cast<int64_t>(a) * p.max_blocks_per_seq + j] : -1;
+  // The table entry is read whatever the length, so that both loads are in flight together
+  // (j is below max_blocks_per_seq whenever that is positive).  The empty tile of a sequence
+  // with no context reads nothing (block id -1) and has 0 tokens.
+  const int entry = p.max_blocks_per_seq > 0 ? p.block_tables[static_cast<int64_t>(a) * p.max_blocks_per_seq + j] : -1;
+  const int phys = L > 0 ? entry : -1;
   const int ntok = min(kBlock, L - j * kBlock);
   return make_int4(phys, a, j, ntok | (j == nblk - 1 ? kLast : 0));
 }
@@ -270,7 +276,7 @@ void decode_sk_kernel(SkParams p) {
     // tile entries: lane i of ent holds tile t0 + kb + i, ent2 the next 64
     int kb = 0;
     int4 ent = lane < n ? tile_entry(p, s_cu, t0 + lane) : make_int4(0, 0, 0, 0);
-    int4 ent2 = lane + 64 < n ? tile_entry(p, s_cu, t0 + 64 + lane) : make_int4(0, 0, 0, 0);
+    int4 ent2;  // read once the first tile's loads are out
 
     const int64_t block_bytes = static_cast<int64_t>(kBlock) * p.num_kv_heads * ROW;
     const int voff = r16 * p.num_kv_heads * ROW + g * ROW + grp * 16;
@@ -317,6 +323,7 @@ void decode_sk_kernel(SkParams p) {
       for (int c = 0; c < KC; ++c) vbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + c * 64, 0, 0);
     };
     issue(0);
+    ent2 = lane + 64 < n ? tile_entry(p, s_cu, t0 + 64 + lane) : make_int4(0, 0, 0, 0);
 
     int cur_s = -1, seg_j0 = 0, seg_k0 = 0;
     typename M::v8 qb[KC];
@@ -485,8 +492,11 @@ void decode_sk_kernel(SkParams p) {
     const int64_t rec = (static_cast<int64_t>(wgr) * p.num_kv_heads + g) * 2 + slot;
     float* pa = p.ws_acc + rec * (16 * D) + r16 * D;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(pa + 16 * c + 4 * grp) = ca[c];
-    if (grp == 0) *reinterpret_cast<float2*>(p.ws_ml + rec * 32 + r16 * 2) = make_float2(cm, cl);
+    for (int c = 0; c < NC; ++c) __builtin_nontemporal_store(ca[c], reinterpret_cast<f32x4*>(pa + 16 * c + 4 * grp));
+    if (grp == 0) {
+      __builtin_nontemporal_store(cm, p.ws_ml + rec * 32 + r16 * 2);
+      __builtin_nontemporal_store(cl, p.ws_ml + rec * 32 + r16 * 2 + 1);
+    }
   };
   for (int sp = 0; sp < kSplits; ++sp) {
     const int w = sp * kHeads + hw;
