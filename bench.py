@@ -105,6 +105,109 @@ def cpu_baseline(w, budget_s=15.0):
                       f"{len(os.sched_getaffinity(0))}"}
 
 
+# Block shape of the default workload's pools: 16 tokens x 8 KV heads x 128 x bf16 = 32 KiB.
+BLOCK_SHAPE = (16, 8, 128)
+PCIE_PEAK_GBS = 64.0  # host link of an MI355X: PCIe 5.0 x16, per direction, vendor figure
+
+
+def _time_calls(fn, steps, warmup, stream):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps / 1e3  # seconds per call
+
+
+def bench_copy_blocks(args, dev):
+    """pkv_copy_blocks on the default workload's block shape: 4096 (source, destination)
+    pairs drawn from a 16384-block pool per call; bytes = pairs x 2 pools x block x (read +
+    write)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_376_amd import binding
+
+    nb, n = 16384, 4096
+    rng = np.random.default_rng(args.seed)
+    k = torch.randn((nb,) + BLOCK_SHAPE, dtype=torch.bfloat16, device=dev)
+    v = torch.randn((nb,) + BLOCK_SHAPE, dtype=torch.bfloat16, device=dev)
+    perm = rng.permutation(nb)
+    pairs = torch.from_numpy(np.stack([perm[:n], perm[n:2 * n]], axis=1).astype(np.int32)).to(dev)
+    stream = torch.cuda.current_stream()
+    block_bytes = int(np.prod(BLOCK_SHAPE)) * 2
+    moved = n * 2 * block_bytes * 2
+    t = _time_calls(lambda: binding.copy_blocks(k, v, pairs, stream=stream), args.steps, args.warmup, stream)
+    gbs = moved / t / 1e9
+    log(f"copy_blocks: {n} pairs of {block_bytes} B blocks per pool, {t * 1e6:.1f} us per call, {gbs:.0f} GB/s")
+    return {"metric": "pkv_copy_blocks (copy-on-write) GB/s, read + write", "value": round(gbs, 2), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t * 1e3, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (copied as bytes)",
+            "data": "synthetic random pools and pairs",
+            "config": {"workload": f"copy_blocks: {n} pairs from a {nb}-block pool, block {BLOCK_SHAPE} bf16",
+                       "bytes_per_call": moved},
+            "roofline": {"kernel": "copy_blocks_kernel", "bound": "hbm", "achieved": round(gbs, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": None, "bytes_per_launch": moved, "avg_launch_us": round(t * 1e6, 2)}}
+
+
+def bench_swap(args, dev):
+    """pkv_swap_blocks between a device pool and a pinned host pool of the default block shape:
+    2048 blocks out (device -> host) and 2048 back in per call; against one copy command per
+    block (what a runtime memcpy per block costs)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_376_amd import binding
+
+    nb, nh, n = 8192, 4096, 2048
+    rng = np.random.default_rng(args.seed)
+    k = torch.randn((nb,) + BLOCK_SHAPE, dtype=torch.bfloat16, device=dev)
+    v = torch.randn((nb,) + BLOCK_SHAPE, dtype=torch.bfloat16, device=dev)
+    hk = torch.empty((nh,) + BLOCK_SHAPE, dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty((nh,) + BLOCK_SHAPE, dtype=torch.bfloat16).pin_memory()
+    dev_ids = rng.permutation(nb)[:n]
+    host_ids = rng.permutation(nh)[:n]
+    out_pairs = torch.from_numpy(np.stack([dev_ids, host_ids], axis=1).astype(np.int32)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([host_ids, dev_ids], axis=1).astype(np.int32)).to(dev)
+    stream = torch.cuda.current_stream()
+    block_bytes = int(np.prod(BLOCK_SHAPE)) * 2
+    moved = n * 2 * block_bytes  # bytes over the link per direction per call
+    steps = max(3, args.steps // 5)
+    t_out = _time_calls(lambda: binding.swap_blocks(hk, hv, k, v, out_pairs, stream=stream), steps, 2, stream)
+    t_in = _time_calls(lambda: binding.swap_blocks(k, v, hk, hv, in_pairs, stream=stream), steps, 2, stream)
+    ids_d, ids_h = dev_ids.tolist(), host_ids.tolist()
+
+    def per_block_out():
+        for a, b in zip(ids_d, ids_h):
+            hk[b].copy_(k[a], non_blocking=True)
+            hv[b].copy_(v[a], non_blocking=True)
+
+    t_ref = _time_calls(per_block_out, 2, 1, stream)
+    g_out, g_in, g_ref = moved / t_out / 1e9, moved / t_in / 1e9, moved / t_ref / 1e9
+    log(f"swap: {n} blocks x 2 pools ({moved / 1e6:.0f} MB) out {t_out * 1e3:.2f} ms ({g_out:.1f} GB/s), "
+        f"in {t_in * 1e3:.2f} ms ({g_in:.1f} GB/s); one copy command per block: {t_ref * 1e3:.2f} ms ({g_ref:.1f} GB/s)")
+    return {"metric": "pkv_swap_blocks device<->pinned host GB/s (out, in)", "value": round(min(g_out, g_in), 2),
+            "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": 2,
+            "ms_per_step": round((t_out + t_in) * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16 (copied as bytes)", "data": "synthetic random pools and pairs",
+            "swap_out_gbs": round(g_out, 2), "swap_in_gbs": round(g_in, 2),
+            "per_block_copy_commands_out_gbs": round(g_ref, 2),
+            "config": {"workload": f"swap: {n} blocks of {BLOCK_SHAPE} bf16 per pool, K and V, device pool {nb} "
+                                   f"blocks, pinned host pool {nh} blocks", "bytes_per_call": moved},
+            "roofline": {"kernel": "copy_blocks_kernel (host side pinned)", "bound": "pcie",
+                         "achieved": round(min(g_out, g_in), 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(min(g_out, g_in) / PCIE_PEAK_GBS, 4), "traffic": None,
+                         "bytes_per_launch": moved, "avg_launch_us": round((t_out + t_in) / 2 * 1e6, 2)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +223,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--op", choices=["step", "copy_blocks", "swap"], default="step",
+                    help="step: the decode step (default); copy_blocks: pkv_copy_blocks "
+                         "(copy-on-write) GB/s; swap: pkv_swap_blocks device<->pinned host GB/s")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -138,6 +244,10 @@ def main():
     binding.lib()
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.op != "step":
+        result = (bench_copy_blocks if args.op == "copy_blocks" else bench_swap)(args, dev)
+        print(json.dumps(result), flush=True)
+        return
 
     log(f"generating workload {args.config} seed {args.seed}")
     w = workloads.make_workload(args.config, args.seed)

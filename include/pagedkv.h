@@ -217,6 +217,62 @@ PKV_API pkv_status pkv_paged_attn_decode_append(void* out, const void* q,
                                         int32_t partition_size, void* stream);
 
 /* ------------------------------------------------------------------------------------ */
+/* Device: whole-block copies (copy-on-write, swap)                                      */
+/* ------------------------------------------------------------------------------------ */
+
+/* Copies whole blocks inside both pools: for each pair i, block pairs[2i] (source) is copied
+ * onto block pairs[2i+1] (destination) in k_cache and in v_cache, bit for bit, all pairs in
+ * one launch.
+ *
+ * This is the copy half of copy-on-write ([gtnt] §2.2, with the reference counts of §2.1):
+ * before a sequence writes into a partly filled block it shares with others, it takes a fresh
+ * block holding a copy.  pkv_seq_extend decides and reports the (source, destination) pairs;
+ * the copies must run before the append that writes into the destinations.
+ *
+ *   k_cache, v_cache  device pools [num_blocks][block_size][num_kv_heads][head_dim], 16-byte
+ *                     aligned, written at the destination blocks only
+ *   cache             host descriptor (any dtype; block_size, num_kv_heads, head_dim > 0 with
+ *                     a block of a multiple of 16 bytes)
+ *   pairs             device int32 [num_pairs][2] (source, destination), 4-byte aligned
+ *   num_pairs         >= 0 (0 is a no-op)
+ * Pairs with an id outside [0, num_blocks), or with source == destination, are skipped
+ * without any memory access.  A block that is the destination of one pair and the source or
+ * destination of another in the same call races (undefined contents).
+ * Errors: INVALID_ARGUMENT (null or misaligned pointer, num_pairs < 0, bad descriptor),
+ * UNSUPPORTED (dtype, block of a size not a multiple of 16), HIP (launch failed). */
+PKV_API pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* cache,
+                           const int32_t* pairs, int32_t num_pairs, void* stream);
+
+/* Copies whole blocks from one pair of pools into another pair of pools of the same block
+ * shape: for each pair i, block pairs[2i] of (src_k, src_v) onto block pairs[2i+1] of
+ * (dst_k, dst_v), bit for bit, in one launch.
+ *
+ * This moves the bytes of a swap: when device memory runs short, some requests' KV cache goes
+ * out to host memory and comes back once memory frees up (the swap space of [yunthe] section
+ * "生产部署注意事项"); here a sequence's blocks are moved whole, by block id.  Either
+ * side may be device memory or pinned host memory that the GPU can address (for example a
+ * PyTorch tensor made with pin_memory=True); both are read and written by the GPU over the
+ * bus, one kernel per call.
+ *
+ *   dst_k, dst_v       destination pools (dst_num_blocks blocks each), 16-byte aligned
+ *   src_k, src_v       source pools (src_num_blocks blocks each), 16-byte aligned, read only
+ *   cache              host descriptor of the block shape (its num_blocks is not used)
+ *   pairs              int32 [num_pairs][2] (source block, destination block), 4-byte
+ *                      aligned, in device memory or GPU-addressable pinned host memory
+ *   num_pairs          >= 0 (0 is a no-op)
+ * Pairs with an id outside its pool are skipped.  The destination and source pools must be
+ * different allocations (use pkv_copy_blocks inside one pool).  A destination block named
+ * twice races.  The call checks with the HIP runtime that every pointer is device memory or
+ * pinned host memory mapped for the current device.
+ * Errors: INVALID_ARGUMENT (null, misaligned or unmapped pointer, same pool on both sides,
+ * pool size <= 0, num_pairs < 0, bad descriptor), UNSUPPORTED (as pkv_copy_blocks),
+ * HIP (launch failed). */
+PKV_API pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int32_t dst_num_blocks,
+                           const void* src_k, const void* src_v, int32_t src_num_blocks,
+                           const pkv_cache_desc* cache, const int32_t* pairs,
+                           int32_t num_pairs, void* stream);
+
+/* ------------------------------------------------------------------------------------ */
 /* Host: block pool and block tables                                                     */
 /* ------------------------------------------------------------------------------------ */
 

@@ -23,6 +23,7 @@ Modules:
 * ``kv_append``     -- the append scatter and the block-table gather, written from the
                        layout definition.
 * ``block_manager`` -- a pure-Python model of the block pool / block tables.
+* ``block_copy``    -- whole-block copies: copy-on-write inside a pool, swap between pools.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against brute force, closed
 forms, an independent library routine and hand-worked fixtures in ``tests/golden/``.
@@ -31,6 +32,7 @@ forms, an independent library routine and hand-worked fixtures in ``tests/golden
 from .attention import decode_attention, decode_attention_single
 from .kv_append import kv_cache_append, gather_sequence
 from .block_manager import BlockManager, OutOfBlocks
+from .block_copy import copy_blocks, swap_blocks
 
 __all__ = [
     "decode_attention",
@@ -39,4 +41,6 @@ __all__ = [
     "gather_sequence",
     "BlockManager",
     "OutOfBlocks",
+    "copy_blocks",
+    "swap_blocks",
 ]

@@ -42,6 +42,8 @@ SIGNATURES = {
                                      ctypes.c_float, _P, ctypes.c_size_t, _I32, _P]),
     "pkv_paged_attn_decode_append": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32,
                                             _I32, ctypes.c_float, _P, ctypes.c_size_t, _I32, _P]),
+    "pkv_copy_blocks": (_I32, [_P, _P, _P, _P, _I32, _P]),
+    "pkv_swap_blocks": (_I32, [_P, _P, _I32, _P, _P, _I32, _P, _P, _I32, _P]),
     "pkv_pool_create": (_I32, [_I32, _I32, _PI32, ctypes.POINTER(_P)]),
     "pkv_pool_destroy": (None, [_P]),
     "pkv_pool_num_blocks": (_I32, [_P]),
@@ -161,6 +163,38 @@ def kv_cache_append(key, value, k_cache, v_cache, slot_mapping, stream=None) -> 
         raise ValueError("slot_mapping must have T entries")
     _check(lib().pkv_kv_cache_append(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
                                       ctypes.byref(desc), _ptr(slot_mapping), T, _stream(stream)))
+
+
+def _pairs_arg(pairs):
+    import torch
+
+    if pairs.dtype != torch.int32 or not pairs.is_contiguous() or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be a contiguous int32 tensor [n, 2]")
+    return int(pairs.shape[0])
+
+
+def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
+    """pkv_copy_blocks: block pairs[i, 0] onto block pairs[i, 1] in both pools (copy-on-write)."""
+    _same(k_cache, v_cache)
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache shapes differ")
+    n = _pairs_arg(pairs)
+    desc = cache_desc(k_cache)
+    _check(lib().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(pairs), n, _stream(stream)))
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None) -> None:
+    """pkv_swap_blocks: block pairs[i, 0] of (src_k, src_v) onto block pairs[i, 1] of
+    (dst_k, dst_v); either side device memory or pinned host memory."""
+    for a in (dst_k, dst_v, src_k, src_v):
+        if not a.is_contiguous() or a.dtype != dst_k.dtype or tuple(a.shape[1:]) != tuple(dst_k.shape[1:]):
+            raise ValueError("pools must be contiguous with one block shape and dtype")
+    if tuple(dst_v.shape) != tuple(dst_k.shape) or tuple(src_v.shape) != tuple(src_k.shape):
+        raise ValueError("K and V pools of one side differ in shape")
+    n = _pairs_arg(pairs)
+    desc = cache_desc(dst_k)
+    _check(lib().pkv_swap_blocks(_ptr(dst_k), _ptr(dst_v), int(dst_k.shape[0]), _ptr(src_k), _ptr(src_v),
+                                 int(src_k.shape[0]), ctypes.byref(desc), _ptr(pairs), n, _stream(stream)))
 
 
 def paged_attn_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,

@@ -1,8 +1,9 @@
 """A paged KV cache on one device: the host block pool plus the two device pools.
 
 Host bookkeeping (which block, which slot) is the C++ pool behind ``binding.BlockPool``;
-every byte written into the device pools goes through ``pkv_kv_cache_append``.  torch
-provides the device memory (and the block copies of copy-on-write).
+every byte written into the device pools goes through the library: rows through
+``pkv_kv_cache_append``, copy-on-write block copies through ``pkv_copy_blocks``.  torch only
+provides the device memory.
 """
 
 from __future__ import annotations
@@ -45,10 +46,14 @@ class PagedKVCache:
             binding.kv_cache_append(k, v, self.k_cache, self.v_cache, sl)
 
     def copy_blocks(self, pairs) -> None:
-        """Copy-on-write: duplicate block src into dst in both pools."""
-        for src, dst in pairs:
-            self.k_cache[dst].copy_(self.k_cache[src])
-            self.v_cache[dst].copy_(self.v_cache[src])
+        """Copy-on-write: duplicate block src into dst in both pools (pkv_copy_blocks, one launch)."""
+        import torch
+
+        pairs = list(pairs)
+        if not pairs:
+            return
+        t = torch.tensor(pairs, dtype=torch.int32).reshape(-1, 2).to(self.device)
+        binding.copy_blocks(self.k_cache, self.v_cache, t)
 
     # ---------------------------------------------------------------- sequences
     def add_sequence(self, seq: int, key, value) -> np.ndarray:

@@ -191,14 +191,15 @@ def test_workspace_size_and_partition_rules():
     assert ws(64, 32, 32, 128, 8192, 0) == (0 if P == 1 else 64 * 32 * P * 130 * 4)
     assert ws(4, 4, 4, 64, 100, 0) == 0
     # auto with G > 2: the even split over the GPU has no fixed partition; its workspace
-    # holds per-range records (16 x D fp32 acc + 16 x 2 stats, two per range and KV head)
-    # plus the prefix sum of block counts
+    # holds, per work range, records (16 x D fp32 acc + 16 x 2 stats, two per KV head) and
+    # one 16-byte descriptor
     assert ps(256, 64, 8, 128, 8192, 0) == 0
     w128 = ws(256, 64, 8, 128, 8192, 0)
     w64 = ws(256, 64, 8, 64, 8192, 0)
     rec128, rec64 = 16 * 128 * 4 + 32 * 4, 16 * 64 * 4 + 32 * 4
-    assert w128 > 0 and (w128 - 257 * 4) // rec128 == (w64 - 257 * 4) // rec64
-    assert ((w128 - 257 * 4) // rec128) % (2 * 8) == 0
+    per_range128, per_range64 = 2 * 8 * rec128 + 16, 2 * 8 * rec64 + 16
+    assert w128 > 0 and w128 % per_range128 == 0 and w64 % per_range64 == 0
+    assert w128 // per_range128 == w64 // per_range64  # same number of ranges
     assert ws(256, 64, 8, 128, 8192, 0) == w128  # deterministic
     # tiny contexts: at most one range per 8 worst-case tiles
     assert ws(1, 8, 1, 128, 16, 0) <= 2 * rec128 + 256
@@ -217,3 +218,27 @@ def test_append_rejects_before_launch():
     assert lib.pkv_kv_cache_append(16, 16, 16, 16, ctypes.byref(_desc(d=80)), 16, 3, None) == 2
     assert lib.pkv_kv_cache_append(16, 16, 16, 16, None, 16, 3, None) == 1
     assert lib.pkv_kv_cache_append(16, 16, 16, 16, ctypes.byref(d), 16, 0, None) == 0
+
+
+def test_block_copies_reject_before_launch():
+    lib = B.lib()
+    d = _desc()
+    # pkv_copy_blocks(k, v, desc, pairs, n, stream)
+    assert lib.pkv_copy_blocks(16, 16, ctypes.byref(d), 16, 0, None) == 0       # nothing to copy
+    assert lib.pkv_copy_blocks(16, 16, ctypes.byref(d), 16, -1, None) == 1
+    assert lib.pkv_copy_blocks(None, 16, ctypes.byref(d), 16, 2, None) == 1
+    assert lib.pkv_copy_blocks(16, 16, ctypes.byref(d), None, 2, None) == 1
+    assert lib.pkv_copy_blocks(24, 16, ctypes.byref(d), 16, 2, None) == 1        # misaligned pool
+    assert lib.pkv_copy_blocks(16, 16, ctypes.byref(d), 18, 2, None) == 1        # misaligned pairs
+    assert lib.pkv_copy_blocks(16, 16, None, 16, 2, None) == 1
+    assert lib.pkv_copy_blocks(16, 16, ctypes.byref(_desc(dt=7)), 16, 2, None) == 2
+    assert lib.pkv_copy_blocks(16, 16, ctypes.byref(_desc(nb=0)), 16, 2, None) == 1
+    assert lib.pkv_copy_blocks(16, 16, ctypes.byref(_desc(bs=1, hkv=1, d=3)), 16, 2, None) == 2  # 6-byte block
+    # pkv_swap_blocks(dk, dv, dnb, sk, sv, snb, desc, pairs, n, stream): checks that need no device
+    assert lib.pkv_swap_blocks(16, 32, 4, 48, 64, 4, ctypes.byref(d), 16, 0, None) == 0
+    assert lib.pkv_swap_blocks(16, 32, 4, 48, 64, 4, ctypes.byref(d), 16, -1, None) == 1
+    assert lib.pkv_swap_blocks(16, 32, 0, 48, 64, 4, ctypes.byref(d), 16, 1, None) == 1
+    assert lib.pkv_swap_blocks(16, 32, 4, 16, 64, 4, ctypes.byref(d), 16, 1, None) == 1  # same pool
+    assert lib.pkv_swap_blocks(None, 32, 4, 48, 64, 4, ctypes.byref(d), 16, 1, None) == 1
+    assert lib.pkv_swap_blocks(16, 40, 4, 48, 64, 4, ctypes.byref(d), 16, 1, None) == 1  # misaligned
+    assert lib.pkv_swap_blocks(16, 32, 4, 48, 64, 4, None, 16, 1, None) == 1

@@ -1,0 +1,120 @@
+"""CPU pins of the oracle's whole-block copies (copy-on-write inside a pool, swap between
+pools): a hand-worked fixture, the copy-on-write story of a forked sequence told through the
+block manager and the append/gather oracle, and properties on random pools."""
+
+import json
+import os
+
+import numpy as np
+from hypothesis import given, settings, strategies as st
+
+import oracle
+from oracle.block_manager import BlockManager
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _fixture():
+    with open(os.path.join(GOLDEN, "block_copy_worked.json"), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def test_copy_matches_hand_worked_fixture():
+    fx = _fixture()
+    k = np.array(fx["k_pool"], dtype=np.float32)
+    v = np.array(fx["v_pool"], dtype=np.float32)
+    nk, nv = oracle.copy_blocks(k, v, fx["copy"]["pairs"])
+    assert np.array_equal(nk, np.array(fx["copy"]["expected_k"], dtype=np.float32))
+    assert np.array_equal(nv, np.array(fx["copy"]["expected_v"], dtype=np.float32))
+    assert np.array_equal(k, np.array(fx["k_pool"], dtype=np.float32))  # input untouched
+    sk, sv = oracle.copy_blocks(k, v, fx["copy_onto_itself"]["pairs"])
+    assert np.array_equal(sk, k) and np.array_equal(sv, v)
+
+
+def test_swap_matches_hand_worked_fixture():
+    fx = _fixture()
+    k = np.array(fx["k_pool"], dtype=np.float32)
+    v = np.array(fx["v_pool"], dtype=np.float32)
+    sw = fx["swap"]
+    dk = np.full((sw["dst_blocks"],) + k.shape[1:], sw["fill"], dtype=np.float32)
+    dv = dk.copy()
+    nk, nv = oracle.swap_blocks(dk, dv, k, v, sw["pairs"])
+    assert np.array_equal(nk, np.array(sw["expected_k"], dtype=np.float32))
+    assert np.array_equal(nv, np.array(sw["expected_v"], dtype=np.float32))
+
+
+def test_copy_on_write_keeps_parent_and_extends_child():
+    """A parent with a partly filled last block is forked; the child appends one token.  The
+    block manager reports one (shared, fresh) pair; after the copy and the child's append the
+    parent reads back its own tokens and the child reads the parent's tokens plus its new one.
+    A missing copy, a reversed copy or a partial copy each break one of these reads."""
+    rng = np.random.default_rng(3)
+    bs, hkv, d = 16, 2, 4
+    bm = BlockManager(8, bs, free_order=rng.permutation(8).tolist())
+    k = np.full((8, bs, hkv, d), np.nan, dtype=np.float32)
+    v = k.copy()
+    parent_k = rng.standard_normal((20, hkv, d)).astype(np.float32)
+    parent_v = rng.standard_normal((20, hkv, d)).astype(np.float32)
+    bm.allocate(0, 0)
+    slots, cows = bm.extend(0, 20)
+    assert cows == []
+    k, v = oracle.kv_cache_append(k, v, parent_k, parent_v, slots, bs)
+    bm.fork(0, 1)
+    new_k = rng.standard_normal((1, hkv, d)).astype(np.float32)
+    new_v = rng.standard_normal((1, hkv, d)).astype(np.float32)
+    slots, cows = bm.extend(1, 1)
+    assert len(cows) == 1
+    src, dst = cows[0]
+    assert bm.block_table(0)[-1] == src and bm.block_table(1)[-1] == dst and src != dst
+    k, v = oracle.copy_blocks(k, v, cows)
+    k, v = oracle.kv_cache_append(k, v, new_k, new_v, slots, bs)
+    got_pk = oracle.gather_sequence(k, bm.block_table(0), bm.context_len(0))
+    got_pv = oracle.gather_sequence(v, bm.block_table(0), bm.context_len(0))
+    assert np.array_equal(got_pk, parent_k) and np.array_equal(got_pv, parent_v)
+    got_ck = oracle.gather_sequence(k, bm.block_table(1), bm.context_len(1))
+    got_cv = oracle.gather_sequence(v, bm.block_table(1), bm.context_len(1))
+    assert np.array_equal(got_ck, np.concatenate([parent_k, new_k]))
+    assert np.array_equal(got_cv, np.concatenate([parent_v, new_v]))
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(min_value=2, max_value=12), st.integers(min_value=0, max_value=2**31 - 1),
+       st.integers(min_value=0, max_value=6))
+def test_copy_properties(nb, seed, n_pairs):
+    """Destinations hold their source's old data; every other block is untouched."""
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((nb, 3, 2, 2)).astype(np.float32)
+    v = rng.standard_normal((nb, 3, 2, 2)).astype(np.float32)
+    perm = rng.permutation(nb).tolist()
+    n = min(n_pairs, nb // 2)
+    srcs, dsts = perm[:n], perm[n:2 * n]  # disjoint: no destination is also a source
+    pairs = list(zip(srcs, dsts))
+    nk, nv = oracle.copy_blocks(k, v, pairs)
+    for b in range(nb):
+        if b in dsts:
+            s = srcs[dsts.index(b)]
+            assert np.array_equal(nk[b], k[s]) and np.array_equal(nv[b], v[s])
+        else:
+            assert np.array_equal(nk[b], k[b]) and np.array_equal(nv[b], v[b])
+
+
+@settings(max_examples=40, deadline=None)
+@given(st.integers(min_value=1, max_value=10), st.integers(min_value=0, max_value=2**31 - 1))
+def test_swap_out_and_back_restores_blocks(nb, seed):
+    """Blocks swapped out to a host pool at fresh ids and back in at other ids read back equal."""
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((nb, 2, 1, 3)).astype(np.float32)
+    v = rng.standard_normal((nb, 2, 1, 3)).astype(np.float32)
+    chosen = rng.permutation(nb)[: rng.integers(1, nb + 1)].tolist()
+    host_ids = rng.permutation(len(chosen) + 3)[: len(chosen)].tolist()
+    k0 = k.copy()
+    hk = np.zeros((len(chosen) + 3,) + k.shape[1:], dtype=np.float32)
+    hv = hk.copy()
+    hk, hv = oracle.swap_blocks(hk, hv, k, v, list(zip(chosen, host_ids)))
+    back_ids = rng.permutation(nb)[: len(chosen)].tolist()
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dk, dv = oracle.swap_blocks(dk, dv, hk, hv, list(zip(host_ids, back_ids)))
+    for c, b in zip(chosen, back_ids):
+        assert np.array_equal(dk[b], k[c]) and np.array_equal(dv[b], v[c])
+    assert np.array_equal(k, k0)  # the source pool is only read
