@@ -327,6 +327,32 @@ PKV_API pkv_status pkv_seq_free(pkv_block_pool* pool, int64_t seq);
 /* Token count of seq, or -1 if unknown. */
 PKV_API int64_t pkv_seq_context_len(const pkv_block_pool* pool, int64_t seq);
 
+/* Moves whole sequences from pool `src` to pool `dst` (for example from the device pool to a
+ * pool in pinned host memory and back): the swap space of [yunthe] section "生产部署注意事项",
+ * where some requests' KV cache goes out to host memory when device memory runs short and
+ * comes back later.  Host bookkeeping only; the bytes move with pkv_swap_blocks.
+ *
+ * The distinct blocks of the listed sequences (first use first: sequences in the given order,
+ * each table in logical order) each take one fresh block of dst, popped from the end of its
+ * free list, which inherits the block's reference count; (src block, dst block) goes to
+ * pairs_out in that order.  The sequences' tables are rewritten through this map and the
+ * sequences leave src exactly as pkv_seq_free would leave it (blocks whose count reaches zero
+ * are pushed onto src's free list in walk order).  Blocks shared only among the moving
+ * sequences stay shared in dst; a block also used by a sequence that does not move is refused.
+ *
+ *   seqs         n distinct sequence ids of src, none present in dst (n >= 0)
+ *   pairs_out    int32 [capacity][2]; receives num_pairs_out pairs (<= the total number of
+ *                blocks in the listed tables)
+ * Copy the pairs' blocks (src pools -> dst pools) before any later write into src's freed
+ * blocks, e.g. by enqueuing pkv_swap_blocks right away on the stream that writes the pools.
+ * Errors (nothing changes): INVALID_ARGUMENT (null pool, same pool, different block sizes,
+ * n < 0, a sequence listed twice, pairs_out too small), NOT_FOUND (sequence not in src),
+ * ALREADY_EXISTS (sequence already in dst), UNSUPPORTED (a block shared with a sequence that
+ * stays), OUT_OF_BLOCKS (dst has too few free blocks). */
+PKV_API pkv_status pkv_pool_move_seqs(pkv_block_pool* src, pkv_block_pool* dst, const int64_t* seqs,
+                              int32_t n, int32_t* pairs_out, int32_t capacity,
+                              int32_t* num_pairs_out);
+
 /* Block tables of seqs[0..n) as rows of tables_out[n][max_blocks_per_seq] (padded with
  * -1) and their context lengths in context_lens_out[n] (both host, nullable each).
  * NOT_FOUND, INVALID_ARGUMENT (a table longer than max_blocks_per_seq). */

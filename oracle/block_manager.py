@@ -31,7 +31,8 @@ Readings where the pages are silent (stated again in the design notes):
   block onto the end of the free list when the count reaches zero;
 * ``fork`` gives the child the parent's table and token count and increments every
   block's count;
-* a slot is ``physical_block * block_size + offset``.
+* a slot is ``physical_block * block_size + offset``;
+* a swap moves whole sequences between two pools (``move_seqs``).
 """
 
 from __future__ import annotations
@@ -39,6 +40,10 @@ from __future__ import annotations
 
 class OutOfBlocks(Exception):
     """The free list cannot cover the request; the pool was left unchanged."""
+
+
+class SharedWithStayingSequence(Exception):
+    """A block of a moving sequence is also used by one that stays; nothing changed."""
 
 
 def _ceil_div(a: int, b: int) -> int:
@@ -156,6 +161,57 @@ class BlockManager:
             if self.ref_count[b] == 0:
                 self.free_blocks.append(b)
         del self.num_tokens[seq]
+
+    def move_seqs(self, dst: "BlockManager", seqs):
+        """Move sequences into another pool (swap out to host, or back in); returns the
+        (block here, block in dst) pairs whose data must be copied.
+
+        The yunthe.com page, section "生产部署注意事项", describes the swap space: when device
+        memory runs short some requests' KV cache is moved to host memory and brought back
+        later.  Read here as whole sequences changing pools, with these steps:
+
+        1. every listed sequence must exist here and not in ``dst``, and be listed once
+           (checked in list order, the first failure reported);
+        2. the distinct blocks of their tables are numbered in order of first use (sequences
+           in the given order, each table in logical order); each must be referenced only by
+           the moving sequences (a block shared with a sequence that stays cannot move);
+        3. ``dst`` must have a free block for each of them, else nothing changes;
+        4. each such block takes a block popped from the end of ``dst``'s free list, which
+           keeps its reference count; the moved tables are rewritten through this map;
+        5. the sequences then leave this pool exactly as ``free`` would take them out.
+        """
+        seqs = [int(x) for x in seqs]
+        if dst is self or dst.block_size != self.block_size:
+            raise ValueError("destination must be another pool with the same block size")
+        for i, s in enumerate(seqs):  # checked in list order
+            if s not in self.block_tables:
+                raise KeyError(f"unknown sequence {s}")
+            if s in dst.block_tables:
+                raise KeyError(f"sequence {s} already exists in the destination")
+            if s in seqs[:i]:
+                raise ValueError(f"sequence {s} is listed twice")
+        first_use, count = [], {}
+        for s in seqs:
+            for b in self.block_tables[s]:
+                if b not in count:
+                    first_use.append(b)
+                    count[b] = 0
+                count[b] += 1
+        for b in first_use:
+            if self.ref_count[b] != count[b]:
+                raise SharedWithStayingSequence(f"block {b} is also used by a sequence that stays")
+        if len(first_use) > len(dst.free_blocks):
+            raise OutOfBlocks(f"need {len(first_use)} blocks, {len(dst.free_blocks)} free")
+        new_id = {}
+        for b in first_use:
+            nb = dst.free_blocks.pop()
+            dst.ref_count[nb] = self.ref_count[b]
+            new_id[b] = nb
+        for s in seqs:
+            dst.block_tables[s] = [new_id[b] for b in self.block_tables[s]]
+            dst.num_tokens[s] = self.num_tokens[s]
+            self.free(s)
+        return [(b, new_id[b]) for b in first_use]
 
     def tables(self, seqs, max_blocks_per_seq: int):
         """Padded table rows (pad -1) and context lengths for ``seqs``, in that order."""

@@ -44,6 +44,7 @@ SIGNATURES = {
                                             _I32, ctypes.c_float, _P, ctypes.c_size_t, _I32, _P]),
     "pkv_copy_blocks": (_I32, [_P, _P, _P, _P, _I32, _P]),
     "pkv_swap_blocks": (_I32, [_P, _P, _I32, _P, _P, _I32, _P, _P, _I32, _P]),
+    "pkv_pool_move_seqs": (_I32, [_P, _P, _PI64, _I32, _PI32, _I32, _PI32]),
     "pkv_pool_create": (_I32, [_I32, _I32, _PI32, ctypes.POINTER(_P)]),
     "pkv_pool_destroy": (None, [_P]),
     "pkv_pool_num_blocks": (_I32, [_P]),
@@ -338,6 +339,17 @@ class BlockPool:
 
     def seq_free(self, seq: int) -> None:
         _check(lib().pkv_seq_free(self._h, seq))
+
+    def move_seqs(self, dst: "BlockPool", seqs) -> np.ndarray:
+        """pkv_pool_move_seqs: move ``seqs`` into pool ``dst``; returns the (src block, dst
+        block) pairs to copy, int32 [k, 2]."""
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        cap = sum(-(-max(self.seq_context_len(int(x)), 0) // self.block_size) for x in s.tolist())
+        pairs = np.zeros((max(cap, 1), 2), dtype=np.int32)
+        npairs = ctypes.c_int32(0)
+        _check(lib().pkv_pool_move_seqs(self._h, dst._h, s.ctypes.data_as(_PI64), s.size,
+                                        pairs.ctypes.data_as(_PI32), cap, ctypes.byref(npairs)))
+        return pairs[:npairs.value]
 
     def seq_context_len(self, seq: int) -> int:
         return int(lib().pkv_seq_context_len(self._h, seq))

@@ -17,17 +17,22 @@ _PREFIX_BASE = 1 << 40  # sequence ids used for shared prefixes while building g
 
 class PagedKVCache:
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device,
-                 free_order=None, block_size: int = 16, fill=None):
+                 free_order=None, block_size: int = 16, fill=None, pinned: bool = False):
+        """``pinned``: the pools live in pinned host memory (device must be "cpu"), e.g. as the
+        swap space that ``move_to`` moves sequences into and out of."""
         import torch
 
         self.pool = binding.BlockPool(num_blocks, block_size, free_order)
         shape = (num_blocks, block_size, num_kv_heads, head_dim)
+        if pinned and str(device) != "cpu":
+            raise ValueError("pinned pools live on the host (device='cpu')")
+        mk = dict(dtype=dtype, device=device, pin_memory=pinned)
         if fill is None:
-            self.k_cache = torch.empty(shape, dtype=dtype, device=device)
-            self.v_cache = torch.empty(shape, dtype=dtype, device=device)
+            self.k_cache = torch.empty(shape, **mk)
+            self.v_cache = torch.empty(shape, **mk)
         else:
-            self.k_cache = torch.full(shape, fill, dtype=dtype, device=device)
-            self.v_cache = torch.full(shape, fill, dtype=dtype, device=device)
+            self.k_cache = torch.full(shape, fill, **mk)
+            self.v_cache = torch.full(shape, fill, **mk)
         self.block_size = block_size
         self.device = device
 
@@ -67,6 +72,20 @@ class PagedKVCache:
         if len(slots):
             self.write(slots, key, value)
         return slots
+
+    def move_to(self, other: "PagedKVCache", seqs) -> np.ndarray:
+        """Swap: move whole sequences into ``other`` (device pools <-> pinned host pools).  The
+        host pools do the bookkeeping (pkv_pool_move_seqs) and one pkv_swap_blocks launch
+        moves the blocks, enqueued before anything can reuse the freed blocks.  Returns the
+        (block here, block there) pairs."""
+        import torch
+
+        pairs = self.pool.move_seqs(other.pool, seqs)
+        if len(pairs):
+            gpu = self.device if str(self.device) != "cpu" else other.device
+            binding.swap_blocks(other.k_cache, other.v_cache, self.k_cache, self.v_cache,
+                                torch.from_numpy(np.ascontiguousarray(pairs)).to(gpu))
+        return pairs
 
     def fork(self, parent: int, child: int) -> None:
         self.pool.seq_fork(parent, child)

@@ -14,6 +14,7 @@
 #include <cstring>
 #include <new>
 #include <unordered_map>
+#include <unordered_set>
 #include <vector>
 
 #include "pkv_internal.h"
@@ -224,5 +225,69 @@ extern "C" pkv_status pkv_pool_block_tables(const pkv_block_pool* p, const int64
     }
     if (context_lens_out) context_lens_out[i] = static_cast<int32_t>(s.num_tokens);
   }
+  return PKV_OK;
+}
+
+// Swap of whole sequences between two pools (the swap space of the yunthe.com page, section
+// "生产部署注意事项": KV cache moved out to host memory when device memory runs short and back
+// later).  The moved sequences' distinct blocks, in order of first use (sequences in the given
+// order, each table in logical order), each get one fresh block of `dst`, popped from the end
+// of its free list, that inherits the block's reference count; the sequences' tables are
+// rewritten through that map and the sequences leave `src` as pkv_seq_free would leave it.
+extern "C" pkv_status pkv_pool_move_seqs(pkv_block_pool* src, pkv_block_pool* dst, const int64_t* seqs, int32_t n,
+                                         int32_t* pairs_out, int32_t capacity, int32_t* num_pairs_out) {
+  pkv::clear_error();
+  if (num_pairs_out) *num_pairs_out = 0;
+  if (!src || !dst) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "pool is NULL");
+  if (src == dst) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "source and destination are the same pool");
+  if (src->block_size != dst->block_size)
+    return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "block sizes differ (%d, %d)", src->block_size, dst->block_size);
+  if (n < 0 || (n > 0 && !seqs)) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "n=%d seqs=%p", n, (const void*)seqs);
+  if (capacity < 0) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "capacity=%d", capacity);
+  // validate everything before changing anything
+  std::unordered_set<int64_t> seen;
+  std::unordered_map<int32_t, int32_t> uses;  // block -> references held by the moving sequences
+  std::vector<int32_t> order;                  // distinct blocks, first use first
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = src->seqs.find(seqs[i]);
+    if (it == src->seqs.end()) return pkv::fail(PKV_ERR_NOT_FOUND, "sequence %lld", (long long)seqs[i]);
+    if (dst->seqs.count(seqs[i]))
+      return pkv::fail(PKV_ERR_ALREADY_EXISTS, "sequence %lld exists in the destination", (long long)seqs[i]);
+    if (!seen.insert(seqs[i]).second)
+      return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "sequence %lld listed twice", (long long)seqs[i]);
+    for (int32_t b : it->second.table)
+      if (uses[b]++ == 0) order.push_back(b);
+  }
+  for (int32_t b : order)
+    if (src->ref[b] != uses[b])
+      return pkv::fail(PKV_ERR_UNSUPPORTED, "block %d is also used by a sequence that does not move", b);
+  if (order.size() > dst->free_list.size())
+    return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "need %zu blocks, %zu free", order.size(), dst->free_list.size());
+  if (static_cast<int64_t>(order.size()) > capacity || (!pairs_out && !order.empty()))
+    return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "pairs_out holds %d pairs, %zu needed", pairs_out ? capacity : 0,
+                     order.size());
+  std::unordered_map<int32_t, int32_t> to;
+  for (size_t k = 0; k < order.size(); ++k) {
+    const int32_t b = order[k];
+    const int32_t nb = dst->free_list.back();
+    dst->free_list.pop_back();
+    dst->ref[nb] = uses[b];
+    to[b] = nb;
+    pairs_out[2 * k] = b;
+    pairs_out[2 * k + 1] = nb;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = src->seqs.find(seqs[i]);
+    pkv_block_pool::Seq moved;
+    moved.num_tokens = it->second.num_tokens;
+    moved.table.reserve(it->second.table.size());
+    for (int32_t b : it->second.table) {
+      moved.table.push_back(to[b]);
+      if (--src->ref[b] == 0) src->free_list.push_back(b);
+    }
+    src->seqs.erase(it);
+    dst->seqs.emplace(seqs[i], std::move(moved));
+  }
+  if (num_pairs_out) *num_pairs_out = static_cast<int32_t>(order.size());
   return PKV_OK;
 }

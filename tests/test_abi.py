@@ -115,6 +115,103 @@ def test_pool_matches_oracle_on_random_histories(ops, nb, bs, seed):
         _same_state(pool, bm)
 
 
+def _move_both(pools, bms, src, seqs):
+    """Move ``seqs`` from pool index src to the other one in the C++ pools and in the oracle."""
+    from oracle.block_manager import SharedWithStayingSequence
+
+    dst = 1 - src
+    res_c = res_o = err_c = err_o = None
+    try:
+        res_c = pools[src].move_seqs(pools[dst], seqs).tolist()
+    except B.PkvError as e:
+        err_c = e.status_name
+    try:
+        res_o = [list(p) for p in bms[src].move_seqs(bms[dst], seqs)]
+    except OracleOOB:
+        err_o = "PKV_ERR_OUT_OF_BLOCKS"
+    except SharedWithStayingSequence:
+        err_o = "PKV_ERR_UNSUPPORTED"
+    except KeyError as e:
+        err_o = "PKV_ERR_ALREADY_EXISTS" if "exists" in str(e) else "PKV_ERR_NOT_FOUND"
+    except ValueError:
+        err_o = "PKV_ERR_INVALID_ARGUMENT"
+    assert err_c == err_o, (src, seqs, err_c, err_o)
+    assert res_c == res_o, (src, seqs, res_c, res_o)
+
+
+def test_move_seqs_replays_hand_worked_swap():
+    with open(os.path.join(ROOT, "tests", "golden", "block_swap_worked.json"), encoding="utf-8") as f:
+        fx = json.load(f)
+    dp, hp = fx["device_pool"], fx["host_pool"]
+    pools = [B.BlockPool(dp["num_blocks"], dp["block_size"], dp["free_order"]),
+             B.BlockPool(hp["num_blocks"], hp["block_size"], hp["free_order"])]
+    bms = [BlockManager(dp["num_blocks"], dp["block_size"], dp["free_order"]),
+           BlockManager(hp["num_blocks"], hp["block_size"], hp["free_order"])]
+    for op in fx["setup"]:
+        tup = {"allocate": ("allocate", op.get("seq"), 0, op.get("tokens", 0)),
+               "fork": ("fork", op.get("parent"), op.get("child"), 0),
+               "extend": ("extend", op.get("seq"), 0, op.get("n", 0))}[op["op"]]
+        _both_run(pools[0], bms[0], tup)
+    with pytest.raises(B.PkvError) as e:
+        pools[0].move_seqs(pools[1], fx["refused"]["seqs"])
+    assert e.value.status_name == "PKV_ERR_UNSUPPORTED"
+    _same_state(pools[0], bms[0])
+    assert pools[0].move_seqs(pools[1], fx["out"]["seqs"]).tolist() == fx["out"]["expected_pairs"]
+    assert pools[1].free_list() == fx["out"]["expected_host_free"]
+    assert pools[0].free_list() == fx["out"]["expected_device_free"]
+    assert pools[1].block_tables([1, 2], 2)[0].tolist() == [fx["out"]["expected_host_tables"]["1"],
+                                                             fx["out"]["expected_host_tables"]["2"]]
+    assert pools[1].move_seqs(pools[0], fx["back"]["seqs"]).tolist() == fx["back"]["expected_pairs"]
+    assert pools[0].free_list() == fx["back"]["expected_device_free"]
+    assert pools[1].free_list() == fx["back"]["expected_host_free"]
+
+
+_swap_ops = st.lists(st.tuples(st.sampled_from(["allocate", "extend", "fork", "free", "move"]),
+                               st.integers(0, 5), st.integers(0, 5), st.integers(0, 30),
+                               st.lists(st.integers(0, 5), max_size=3), st.integers(0, 1)), max_size=50)
+
+
+@settings(max_examples=300, deadline=None)
+@given(ops=_swap_ops, nb=st.integers(1, 20), nh=st.integers(1, 20), bs=st.sampled_from([1, 4, 16]),
+       seed=st.integers(0, 1000))
+def test_move_seqs_matches_oracle_on_random_histories(ops, nb, nh, bs, seed):
+    """Two pools (device-like, host-like) driven by random histories that move sequence sets
+    back and forth: results, errors and the whole state of both pools match the oracle."""
+    rng = np.random.default_rng(seed)
+    o1, o2 = rng.permutation(nb).astype(np.int32), rng.permutation(nh).astype(np.int32)
+    pools = [B.BlockPool(nb, bs, o1), B.BlockPool(nh, bs, o2)]
+    bms = [BlockManager(nb, bs, o1.tolist()), BlockManager(nh, bs, o2.tolist())]
+    for kind, a, b, n, seqs, side in ops:
+        if kind == "move":
+            _move_both(pools, bms, side, seqs)
+        else:
+            _both_run(pools[side], bms[side], (kind, a, b, n))
+        _same_state(pools[0], bms[0])
+        _same_state(pools[1], bms[1])
+
+
+def test_move_seqs_rejects_bad_arguments():
+    a, b = B.BlockPool(4, 16), B.BlockPool(4, 8)
+    lib = B.lib()
+    n = ctypes.c_int32(0)
+    assert lib.pkv_pool_move_seqs(a._h, a._h, None, 0, None, 0, ctypes.byref(n)) == 1      # same pool
+    assert lib.pkv_pool_move_seqs(a._h, b._h, None, 0, None, 0, ctypes.byref(n)) == 1      # block sizes differ
+    c = B.BlockPool(4, 16)
+    assert lib.pkv_pool_move_seqs(a._h, c._h, None, 0, None, 0, ctypes.byref(n)) == 0      # nothing to move
+    a.seq_allocate(7, 40)
+    seqs = np.array([7], dtype=np.int64)
+    pairs = np.zeros((4, 2), dtype=np.int32)
+    ps = seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    pp = pairs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert lib.pkv_pool_move_seqs(a._h, c._h, ps, 1, pp, 2, ctypes.byref(n)) == 1          # 3 pairs needed
+    assert a.seq_context_len(7) == 40 and c.num_free() == 4                                 # unchanged
+    twice = np.array([7, 7], dtype=np.int64)
+    assert lib.pkv_pool_move_seqs(a._h, c._h, twice.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 2, pp, 4,
+                                  ctypes.byref(n)) == 1
+    assert lib.pkv_pool_move_seqs(a._h, c._h, ps, 1, pp, 4, ctypes.byref(n)) == 0 and n.value == 3
+    assert a.num_free() == 4 and c.seq_context_len(7) == 40
+
+
 def test_pool_rejects_bad_free_order_and_sizes():
     with pytest.raises(B.PkvError) as e:
         B.BlockPool(4, 16, [0, 1, 1, 3])

@@ -157,3 +157,46 @@ def test_swap_refuses_pageable_host_memory():
     assert ei.value.status == 1
     torch.cuda.synchronize()
     assert torch.count_nonzero(kd).item() == 0 and torch.count_nonzero(vd).item() == 0
+
+
+def test_sequences_swap_out_and_back_decode_bitwise_equal():
+    """Sequences (two of them sharing a forked prefix) move to a pinned host cache, their device
+    blocks are reused and overwritten by another sequence, and they move back to other block
+    ids: decode gives bit-for-bit the output from before (the block-relabel invariance), which
+    also matches the attention oracle."""
+    say("[swap seqs] out, overwrite, back, decode")
+    rng = np.random.default_rng(25)
+    tdt, hq, hkv, d = torch.bfloat16, 16, 2, 128
+    dev = PagedKVCache(64, hkv, d, tdt, DEVICE, free_order=rng.permutation(64).astype(np.int32), fill=float("nan"))
+    host = PagedKVCache(48, hkv, d, tdt, "cpu", free_order=rng.permutation(48).astype(np.int32), fill=float("nan"),
+                        pinned=True)
+    kv = {}
+    for s, L in ((0, 50), (1, 200), (2, 17)):
+        k = torch.from_numpy(rng.standard_normal((L, hkv, d), dtype=np.float32)).to(tdt)
+        v = torch.from_numpy(rng.standard_normal((L, hkv, d), dtype=np.float32)).to(tdt)
+        dev.add_sequence(s, k, v)
+        kv[s] = (k, v)
+    dev.fork(1, 3)  # 3 shares 1's 13 blocks; its own token goes through copy-on-write
+    kn = torch.from_numpy(rng.standard_normal((5, hkv, d), dtype=np.float32)).to(tdt)
+    vn = torch.from_numpy(rng.standard_normal((5, hkv, d), dtype=np.float32)).to(tdt)
+    dev.extend(3, kn, vn)
+    kv[3] = (torch.cat([kv[1][0], kn]), torch.cat([kv[1][1], vn]))
+    seqs = [0, 1, 2, 3]
+    q = torch.from_numpy(rng.standard_normal((4, hq, d), dtype=np.float32)).to(tdt)
+    bt, ctx, maxc = dev.tables(seqs)
+    first = decode(dev, q, bt, ctx, maxc, 0.088, 0)
+    pairs = dev.move_to(host, [1, 3, 2])
+    assert len(pairs) == 13 + 1 + 2 and dev.pool.num_seqs() == 1
+    junk = torch.full((600, hkv, d), 3.0, dtype=tdt)  # takes (and overwrites) the freed blocks
+    dev.add_sequence(9, junk, junk)
+    dev.pool.seq_free(9)
+    back = host.move_to(dev, [3, 1, 2])
+    assert len(back) == len(pairs) and host.pool.num_seqs() == 0
+    bt2, ctx2, maxc2 = dev.tables(seqs)
+    assert not torch.equal(bt2.cpu(), bt.cpu())  # other physical blocks
+    second = decode(dev, q, bt2, ctx2, maxc2, 0.088, 0)
+    assert torch.equal(first.view(torch.int16), second.view(torch.int16))
+    ref = oracle.decode_attention(q, [kv[s][0] for s in seqs], [kv[s][1] for s in seqs], 0.088)
+    err = max_err(second, ref)
+    say(f"    max abs err {err:.3e}")
+    assert err <= TOL["bfloat16"]

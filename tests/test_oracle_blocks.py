@@ -118,3 +118,86 @@ def test_swap_out_and_back_restores_blocks(nb, seed):
     for c, b in zip(chosen, back_ids):
         assert np.array_equal(dk[b], k[c]) and np.array_equal(dv[b], v[c])
     assert np.array_equal(k, k0)  # the source pool is only read
+
+
+# ------------------------------------------------------------------ swap of whole sequences
+def _swap_fixture():
+    with open(os.path.join(GOLDEN, "block_swap_worked.json"), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def _setup_pools(fx):
+    d = BlockManager(fx["device_pool"]["num_blocks"], fx["device_pool"]["block_size"], fx["device_pool"]["free_order"])
+    h = BlockManager(fx["host_pool"]["num_blocks"], fx["host_pool"]["block_size"], fx["host_pool"]["free_order"])
+    for op in fx["setup"]:
+        if op["op"] == "allocate":
+            d.allocate(op["seq"], op["tokens"])
+        elif op["op"] == "fork":
+            d.fork(op["parent"], op["child"])
+        else:
+            d.extend(op["seq"], op["n"])
+    return d, h
+
+
+def test_move_seqs_matches_hand_worked_fixture():
+    import pytest
+    from oracle.block_manager import SharedWithStayingSequence
+
+    fx = _swap_fixture()
+    d, h = _setup_pools(fx)
+    with pytest.raises(SharedWithStayingSequence):
+        d.move_seqs(h, fx["refused"]["seqs"])
+    assert d.free_blocks == [0, 1] and h.free_blocks == [0, 1, 2, 3]  # nothing changed
+    out = fx["out"]
+    assert [list(p) for p in d.move_seqs(h, out["seqs"])] == out["expected_pairs"]
+    assert {str(k): v for k, v in h.block_tables.items()} == out["expected_host_tables"]
+    assert {str(b): h.ref_count[b] for b in range(4) if h.ref_count[b]} == out["expected_host_refs"]
+    assert h.free_blocks == out["expected_host_free"] and d.free_blocks == out["expected_device_free"]
+    assert {str(k): v for k, v in d.block_tables.items()} == out["expected_device_tables"]
+    back = fx["back"]
+    assert [list(p) for p in h.move_seqs(d, back["seqs"])] == back["expected_pairs"]
+    assert {str(k): v for k, v in d.block_tables.items()} == back["expected_device_tables"]
+    assert d.free_blocks == back["expected_device_free"] and h.free_blocks == back["expected_host_free"]
+
+
+@settings(max_examples=40, deadline=None)
+@given(st.integers(min_value=0, max_value=2**31 - 1))
+def test_swap_out_and_in_keeps_every_sequence_readable(seed):
+    """Random sequences (some forked, some extended with copy-on-write) swap out to a host pool
+    and back with the block copies of ``swap_blocks``: every sequence gathers the same rows as
+    before, and reference counts match the tables."""
+    rng = np.random.default_rng(seed)
+    bs, hkv, d = 4, 1, 2
+    dev = BlockManager(24, bs, rng.permutation(24).tolist())
+    host = BlockManager(20, bs, rng.permutation(20).tolist())
+    dk = rng.standard_normal((24, bs, hkv, d)).astype(np.float32)
+    dv = rng.standard_normal((24, bs, hkv, d)).astype(np.float32)
+    hk = np.full((20, bs, hkv, d), np.nan, dtype=np.float32)
+    hv = hk.copy()
+    dev.allocate(0, int(rng.integers(1, 9)))
+    dev.fork(0, 1)
+    slots, cows = dev.extend(1, int(rng.integers(0, 3)))
+    dk, dv = oracle.copy_blocks(dk, dv, cows)
+    dev.allocate(2, int(rng.integers(0, 7)))
+    before = {s: (oracle.gather_sequence(dk, dev.block_table(s), dev.context_len(s)),
+                  oracle.gather_sequence(dv, dev.block_table(s), dev.context_len(s))) for s in (0, 1, 2)}
+    moving = [[0, 1], [2], [1, 0, 2]][int(rng.integers(0, 3))]
+    pairs = dev.move_seqs(host, moving)
+    hk, hv = oracle.swap_blocks(hk, hv, dk, dv, pairs)
+    dk = np.where(np.isnan(dk), dk, dk + 1000)  # the device pool's old data is dead once moved
+    dv = np.where(np.isnan(dv), dv, dv + 1000)
+    for s in (0, 1, 2):
+        if s in moving:
+            assert oracle.gather_sequence(hk, host.block_table(s), host.context_len(s)).tolist() == before[s][0].tolist()
+    back = host.move_seqs(dev, moving)
+    dk, dv = oracle.swap_blocks(dk, dv, hk, hv, back)
+    for s in moving:
+        assert np.array_equal(oracle.gather_sequence(dk, dev.block_table(s), dev.context_len(s)), before[s][0])
+        assert np.array_equal(oracle.gather_sequence(dv, dev.block_table(s), dev.context_len(s)), before[s][1])
+    for pool in (dev, host):
+        refs = [0] * pool.num_blocks
+        for t in pool.block_tables.values():
+            for b in t:
+                refs[b] += 1
+        assert refs == pool.ref_count
+        assert sorted(pool.free_blocks + [b for b in range(pool.num_blocks) if refs[b]]) == list(range(pool.num_blocks))
