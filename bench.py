@@ -208,6 +208,49 @@ def bench_swap(args, dev):
                          "bytes_per_launch": moved, "avg_launch_us": round((t_out + t_in) / 2 * 1e6, 2)}}
 
 
+def bench_append(args, dev):
+    """pkv_kv_cache_append of a prefill chunk (multi-token append through the same scatter) into
+    the default workload's pools: T tokens of 8 KV heads x 128 bf16 to the slots of fresh
+    sequences of 1024 tokens taken from the host pool; bytes = T rows x 2 (K, V) x (read +
+    write)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_376_amd import binding
+    from paged_kv_cache_376_amd.cache import PagedKVCache
+
+    T = args.append_tokens
+    bs = args.block_size or 16
+    hkv, d = BLOCK_SHAPE[1], BLOCK_SHAPE[2]
+    nb = -(-T // bs) + 64
+    rng = np.random.default_rng(args.seed)
+    cache = PagedKVCache(nb, hkv, d, torch.bfloat16, dev, free_order=rng.permutation(nb).astype(np.int32),
+                         block_size=bs)
+    slots = []
+    for s in range(-(-T // 1024)):
+        n = min(1024, T - 1024 * s)
+        cache.pool.seq_allocate(s, 0)
+        sl, _ = cache.pool.seq_extend(s, n)
+        slots.append(sl)
+    slot_t = torch.from_numpy(np.concatenate(slots)).to(dev)
+    key = torch.randn((T, hkv, d), dtype=torch.bfloat16, device=dev)
+    value = torch.randn((T, hkv, d), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    moved = T * hkv * d * 2 * 2 * 2
+    t = _time_calls(lambda: binding.kv_cache_append(key, value, cache.k_cache, cache.v_cache, slot_t, stream=stream),
+                    args.steps, args.warmup, stream)
+    gbs = moved / t / 1e9
+    log(f"append: {T} tokens ({hkv}x{d} bf16 per token and pool, block {bs}), {t * 1e6:.1f} us per call, {gbs:.0f} GB/s")
+    return {"metric": "pkv_kv_cache_append (prefill chunk) GB/s, read + write", "value": round(gbs, 2), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t * 1e3, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (copied as bytes)",
+            "data": "synthetic rows, slots of fresh 1024-token sequences",
+            "config": {"workload": f"append: {T} tokens, Hkv {hkv}, D {d}, bf16, block {bs}", "bytes_per_call": moved},
+            "roofline": {"kernel": "kv_append_kernel", "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "bytes_per_launch": moved, "avg_launch_us": round(t * 1e6, 2)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,9 +266,14 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--op", choices=["step", "copy_blocks", "swap"], default="step",
+    ap.add_argument("--op", choices=["step", "copy_blocks", "swap", "append"], default="step",
                     help="step: the decode step (default); copy_blocks: pkv_copy_blocks "
-                         "(copy-on-write) GB/s; swap: pkv_swap_blocks device<->pinned host GB/s")
+                         "(copy-on-write) GB/s; swap: pkv_swap_blocks device<->pinned host GB/s; "
+                         "append: pkv_kv_cache_append of a prefill chunk GB/s")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="tokens per pool block (default: the workload's, 16)")
+    ap.add_argument("--append-tokens", type=int, default=16384,
+                    help="tokens of the prefill chunk for --op append")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -245,12 +293,13 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     if args.op != "step":
-        result = (bench_copy_blocks if args.op == "copy_blocks" else bench_swap)(args, dev)
+        result = {"copy_blocks": bench_copy_blocks, "swap": bench_swap, "append": bench_append}[args.op](args, dev)
         print(json.dumps(result), flush=True)
         return
 
     log(f"generating workload {args.config} seed {args.seed}")
-    w = workloads.make_workload(args.config, args.seed)
+    w = workloads.make_workload(args.config, args.seed,
+                                **({"block_size": args.block_size} if args.block_size else {}))
     sp = w.spec
     t0 = time.perf_counter()
     cache = build_cache(w, dev)
@@ -271,9 +320,9 @@ def main():
     q = w.q.to(dev).contiguous()
     out = torch.empty_like(q)
     part = binding.paged_attn_partition_size(sp.num_seqs, sp.num_q_heads, sp.num_kv_heads,
-                                             sp.head_dim, maxc, args.partition)
+                                             sp.head_dim, maxc, args.partition, sp.dtype)
     ws_bytes = binding.paged_attn_workspace_bytes(sp.num_seqs, sp.num_q_heads, sp.num_kv_heads,
-                                                  sp.head_dim, maxc, args.partition)
+                                                  sp.head_dim, maxc, args.partition, sp.dtype)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -371,7 +420,7 @@ def main():
                       else "pkv_paged_attn_decode_append (append fused into the decode)",
         "config": {
             "workload": f"{sp.name}: paged decode, B={sp.num_seqs}, Hq={sp.num_q_heads}, "
-                        f"Hkv={sp.num_kv_heads}, D={sp.head_dim}, block 16, {sp.dtype}, "
+                        f"Hkv={sp.num_kv_heads}, D={sp.head_dim}, block {sp.block_size}, {sp.dtype}, "
                         f"lengths {sp.lengths}, seed {args.seed}, +1 appended token per sequence",
             "num_seqs": sp.num_seqs,
             "kv_tokens": int(w.context_lens.sum()) + sp.num_seqs,

@@ -27,7 +27,8 @@
  *     kernels are not reported (see each call's device-side contract).
  *   - The library never allocates device memory.
  *   - Host pool calls are not thread-safe: one owner per pool.
- *   - Supported by the kernels: dtype f32, f16, bf16; head_dim 64 or 128; block_size 16.
+ *   - Supported by the kernels: dtype f32, f16, bf16; head_dim 64 or 128; block_size 16
+ *     (decode of f16/bf16 pools also 8 and 32; appends and block copies any block size).
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -101,7 +102,7 @@ PKV_API const char* pkv_version(void);
  * bit; other slots (negative = padding, or out of range) are skipped without any memory
  * access.  Two tokens with the same slot race (undefined which row wins).
  * Errors: INVALID_ARGUMENT (null or misaligned pointer, num_tokens < 0, bad descriptor),
- * UNSUPPORTED (dtype/head_dim/block_size outside the set above), HIP (launch failed). */
+ * UNSUPPORTED (dtype or head_dim outside the set above), HIP (launch failed). */
 PKV_API pkv_status pkv_kv_cache_append(const void* key, const void* value,
                                void* k_cache, void* v_cache, const pkv_cache_desc* cache,
                                const int64_t* slot_mapping, int32_t num_tokens,
@@ -112,27 +113,28 @@ PKV_API pkv_status pkv_kv_cache_append(const void* key, const void* value,
 /* ------------------------------------------------------------------------------------ */
 
 /* Bytes of workspace pkv_paged_attn_decode needs for these arguments (0 when the chosen
- * work split needs none), partition_size as for the decode call.
- *   - partition_size 0 with grouped queries (num_q_heads / num_kv_heads > 2) and at most 8192
- *     sequences: the even split over the GPU; the workspace holds fp32 records of sequences cut
- *     by the split (two per work range and KV head, 16*head_dim + 32 floats each) and the
- *     prefix sum of block counts; it does not depend on the dtype or on the context lengths
- *     beyond max_context_len.
- *   - otherwise: fixed partitions; fp32 partials of split sequences,
- *     num_seqs * num_q_heads * P * (head_dim + 2) floats with P partitions of the longest
- *     context, 0 when nothing is split.
+ * work split needs none), partition_size and dtype (a pkv_dtype) as for the decode call.
+ *   - partition_size 0 with f16/bf16 pools and at most 8192 sequences: the even split over the
+ *     GPU; the workspace holds, per work range, fp32 records of sequences cut by the split (two
+ *     per KV head, 16*head_dim + 32 floats each) and one 16-byte descriptor; it does not
+ *     depend on the context lengths beyond max_context_len nor on the block size.
+ *   - otherwise (f32 pools, or an explicit partition_size): fixed partitions; fp32 partials of
+ *     split sequences, num_seqs * num_q_heads * P * (head_dim + 2) floats with P partitions
+ *     of the longest context, 0 when nothing is split.
  * Returns 0 for arguments the decode call would reject. */
 PKV_API size_t pkv_paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim,
-                                      int32_t max_context_len, int32_t partition_size);
+                                      int32_t max_context_len, int32_t partition_size,
+                                      int32_t dtype);
 
 /* The fixed partition size (tokens) pkv_paged_attn_decode uses for these arguments: the
  * resolved value of partition_size 0 (auto) or -1 (never split: max_context_len rounded up
  * to the block size), or partition_size itself.  0 when the even split over the GPU is used
- * (partition_size 0 with grouped queries, see above) and on invalid arguments. */
+ * (partition_size 0 with f16/bf16 pools, see above) and on invalid arguments. */
 PKV_API int32_t pkv_paged_attn_partition_size(int32_t num_seqs, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim,
-                                      int32_t max_context_len, int32_t partition_size);
+                                      int32_t max_context_len, int32_t partition_size,
+                                      int32_t dtype);
 
 /* Single-query attention of every sequence over its paged context.
  *
@@ -159,12 +161,12 @@ PKV_API int32_t pkv_paged_attn_partition_size(int32_t num_seqs, int32_t num_q_he
  *                  aligned (may be NULL when that is 0); contents on entry and return
  *                  unspecified (no state carries over between calls)
  *   partition_size 0 = auto; -1 = never split; else tokens per partition, a positive
- *                  multiple of block_size.  With 0 and grouped queries (num_q_heads /
- *                  num_kv_heads > 2, f16/bf16, at most 8192 sequences) the work is split
- *                  evenly over the GPU: each KV head's list of (sequence, block) tiles is cut
- *                  into equal ranges whatever the length mix, and sequences cut by the ranges
- *                  are merged exactly (log-sum-exp combine in a fixed order) by a second
- *                  kernel.  Otherwise sequences longer than one partition are processed as
+ *                  multiple of block_size.  With 0 and f16/bf16 pools (at most 8192
+ *                  sequences) the work is split evenly over the GPU: each KV head's list of
+ *                  (sequence, 16-token tile) pairs is cut into equal ranges whatever the
+ *                  length mix, and sequences cut by the ranges are merged exactly (log-sum-exp
+ *                  combine in a fixed order) by a second kernel.  Otherwise (f32 pools, or an
+ *                  explicit size) sequences longer than one partition are processed as
  *                  independent partitions and merged the same way.
  *
  * A sequence with context length 0 yields zeros.  Results are bitwise reproducible run to
@@ -175,6 +177,8 @@ PKV_API int32_t pkv_paged_attn_partition_size(int32_t num_seqs, int32_t num_q_he
  * and table entries in [0, num_blocks).  To never touch memory outside the buffers, the
  * kernels clamp context lengths to max_context_len and skip blocks whose id is out of
  * range; the output is then unspecified, but nothing outside the buffers is read.
+ * Block sizes: 8, 16 or 32 tokens on the even split (f16/bf16, partition_size 0; the block
+ * size of 8 suits models under 7B, [gtnt] end of §6.2); 16 with fixed partitions and for f32.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (dtype/head_dim/block_size/group size outside the
  * implemented set: f32 supports G <= 2, f16/bf16 support G <= 16), WORKSPACE_TOO_SMALL,
  * HIP. */
@@ -195,9 +199,9 @@ PKV_API pkv_status pkv_paged_attn_decode(void* out, const void* q,
  * of [111cn] §3.3 after the host pool has taken that slot (pkv_seq_extend by one token).
  * The result equals pkv_kv_cache_append with those slots followed by pkv_paged_attn_decode,
  * bit for bit in the pools and in the output.  On the evenly split path the wave that
- * reads a sequence's last block takes the new row from new_key/new_value and writes it to
- * the pool itself, so the step is one decode launch plus the merge; otherwise a scatter
- * launch precedes the decode.
+ * reads a sequence's last tile takes the new row from new_key/new_value, and the merge
+ * launch that follows the decode writes the rows to their slots, so the step is the decode
+ * launch plus the merge; otherwise a scatter launch precedes the decode.
  *
  *   new_key, new_value  device [num_seqs][num_kv_heads][head_dim] of cache->dtype, 16-byte
  *                       aligned, read only

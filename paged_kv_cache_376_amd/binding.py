@@ -36,8 +36,8 @@ SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [_I32]),
     "pkv_version": (ctypes.c_char_p, []),
     "pkv_kv_cache_append": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P]),
-    "pkv_paged_attn_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32]),
-    "pkv_paged_attn_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "pkv_paged_attn_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "pkv_paged_attn_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_paged_attn_decode": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32,
                                      ctypes.c_float, _P, ctypes.c_size_t, _I32, _P]),
     "pkv_paged_attn_decode_append": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32,
@@ -198,16 +198,26 @@ def swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None) -> None:
                                  int(src_k.shape[0]), ctypes.byref(desc), _ptr(pairs), n, _stream(stream)))
 
 
+def _dtype_code(dtype) -> int:
+    """pkv_dtype code of a dtype given as a code, a name ("bfloat16") or a torch dtype."""
+    if isinstance(dtype, int):
+        return dtype
+    name = dtype if isinstance(dtype, str) else str(dtype).replace("torch.", "")
+    if name not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {name}")
+    return DTYPE_CODES[name]
+
+
 def paged_attn_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                               partition_size=0) -> int:
+                               partition_size=0, dtype="bfloat16") -> int:
     return int(lib().pkv_paged_attn_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                    max_context_len, partition_size))
+                                                    max_context_len, partition_size, _dtype_code(dtype)))
 
 
 def paged_attn_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                              partition_size=0) -> int:
+                              partition_size=0, dtype="bfloat16") -> int:
     return int(lib().pkv_paged_attn_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                   max_context_len, partition_size))
+                                                   max_context_len, partition_size, _dtype_code(dtype)))
 
 
 def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
@@ -227,7 +237,7 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_
         raise ValueError("block_tables must be contiguous [B, max_blocks_per_seq]")
     if context_lens.numel() != B or not context_lens.is_contiguous():
         raise ValueError("context_lens must be contiguous [B]")
-    need = paged_attn_workspace_bytes(B, Hq, desc.num_kv_heads, D, max_context_len, partition_size)
+    need = paged_attn_workspace_bytes(B, Hq, desc.num_kv_heads, D, max_context_len, partition_size, desc.dtype)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -258,7 +268,7 @@ def paged_attn_decode_append(out, q, new_key, new_value, k_cache, v_cache, block
         raise ValueError("block_tables must be contiguous [B, max_blocks_per_seq]")
     if context_lens.numel() != B or not context_lens.is_contiguous():
         raise ValueError("context_lens must be contiguous [B]")
-    need = paged_attn_workspace_bytes(B, Hq, desc.num_kv_heads, D, max_context_len, partition_size)
+    need = paged_attn_workspace_bytes(B, Hq, desc.num_kv_heads, D, max_context_len, partition_size, desc.dtype)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -106,8 +106,6 @@ extern "C" pkv_status pkv_kv_cache_append(const void* key, const void* value, vo
       cache->block_size <= 0)
     return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "bad cache descriptor (NB=%d bs=%d Hkv=%d D=%d)",
                      cache->num_blocks, cache->block_size, cache->num_kv_heads, cache->head_dim);
-  if (cache->block_size != 16)
-    return pkv::fail(PKV_ERR_UNSUPPORTED, "block_size %d (implemented: 16)", cache->block_size);
   if (cache->head_dim != 64 && cache->head_dim != 128)
     return pkv::fail(PKV_ERR_UNSUPPORTED, "head_dim %d (implemented: 64, 128)", cache->head_dim);
   if (num_tokens == 0) return PKV_OK;

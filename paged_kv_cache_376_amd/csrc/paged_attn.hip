@@ -10,6 +10,10 @@
 // PagedAttention与连续批处理技术解析" §2.1, whose §2.2 also has the kernel work block by
 // block).  Query head h reads KV head h / G, G = Hq / Hkv.
 //
+// This file holds the fixed-partition path (f32 pools, or an explicit partition_size; 16-token
+// blocks) and the entry points; f16/bf16 decodes with partition_size 0 go to the even split of
+// paged_attn_sk.hip.
+//
 // Structure (one decode = phase 1, plus phase 2 only when a sequence is split):
 //   phase 1  grid (Hkv, B, P): one work-group of 4 wave64s per (KV head, sequence,
 //            partition of `part_blocks` blocks).  Wave w streams blocks w, w+4, ... of the
@@ -547,28 +551,33 @@ hipError_t launch_dtype(const Params& p, int D, int G, hipStream_t stream) {
 using namespace pkv;
 
 namespace {
-// The evenly split path serves partition_size 0 for grouped queries (G > 2, which the
-// kernels only implement for 16-bit types) up to kSkMaxSeqs sequences.
-bool use_stream_k(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t partition_size) {
-  return partition_size == 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 &&
-         num_q_heads / num_kv_heads > 2 && num_seqs <= sk::kSkMaxSeqs;
+// The evenly split path (16-bit pools: its products run on the bf16/f16 matrix cores) serves
+// partition_size 0 up to kSkMaxSeqs sequences; f32 pools and explicit partition sizes take
+// the fixed partitions.
+bool use_stream_k(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t partition_size,
+                  int32_t dtype) {
+  return partition_size == 0 && (dtype == PKV_F16 || dtype == PKV_BF16) && num_kv_heads > 0 &&
+         num_q_heads % num_kv_heads == 0 && num_seqs <= sk::kSkMaxSeqs;
 }
 }  // namespace
 
 extern "C" int32_t pkv_paged_attn_partition_size(int32_t num_seqs, int32_t num_q_heads,
                                                  int32_t num_kv_heads, int32_t head_dim,
-                                                 int32_t max_context_len, int32_t partition_size) {
+                                                 int32_t max_context_len, int32_t partition_size,
+                                                 int32_t dtype) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
-  if (max_context_len < 0) return 0;
-  if (use_stream_k(num_seqs, num_q_heads, num_kv_heads, partition_size)) return 0;
+  if (max_context_len < 0 || dtype_bytes(dtype) == 0) return 0;
+  if (use_stream_k(num_seqs, num_q_heads, num_kv_heads, partition_size, dtype)) return 0;
   return resolve_partition(max_context_len, partition_size);
 }
 
 extern "C" size_t pkv_paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                                  int32_t num_kv_heads, int32_t head_dim,
-                                                 int32_t max_context_len, int32_t partition_size) {
+                                                 int32_t max_context_len, int32_t partition_size,
+                                                 int32_t dtype) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
-  if (use_stream_k(num_seqs, num_q_heads, num_kv_heads, partition_size))
+  if (dtype_bytes(dtype) == 0) return 0;
+  if (use_stream_k(num_seqs, num_q_heads, num_kv_heads, partition_size, dtype))
     return num_seqs == 0 ? 0 : sk::sk_workspace_bytes(num_seqs, num_kv_heads, head_dim, max_context_len);
   const int32_t part = resolve_partition(max_context_len, partition_size);
   if (part == 0) return 0;
@@ -597,8 +606,6 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
   if (cache->num_blocks <= 0 || cache->num_kv_heads <= 0 || cache->head_dim <= 0 || cache->block_size <= 0)
     return fail(PKV_ERR_INVALID_ARGUMENT, "bad cache descriptor (NB=%d bs=%d Hkv=%d D=%d)",
                 cache->num_blocks, cache->block_size, cache->num_kv_heads, cache->head_dim);
-  if (cache->block_size != kBlock)
-    return fail(PKV_ERR_UNSUPPORTED, "block_size %d (implemented: 16)", cache->block_size);
   const int D = cache->head_dim;
   if (D != 64 && D != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (implemented: 64, 128)", D);
   if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARGUMENT, "num_seqs=%d", num_seqs);
@@ -608,12 +615,16 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
   const int G = num_q_heads / cache->num_kv_heads;
   if (cache->dtype == PKV_F32 ? G > 2 : G > 16)
     return fail(PKV_ERR_UNSUPPORTED, "group size %d for dtype %d (f32: <= 2, f16/bf16: <= 16)", G, cache->dtype);
+  const bool sk_path = use_stream_k(num_seqs, num_q_heads, cache->num_kv_heads, partition_size, cache->dtype);
+  const int BS = cache->block_size;
+  if (sk_path ? (BS != 8 && BS != 16 && BS != 32) : BS != kBlock)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d (implemented: 8, 16, 32 for f16/bf16 with partition_size 0; "
+                "16 otherwise)", BS);
   if (max_blocks_per_seq < 0 || max_context_len < 0 ||
-      static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBlock)
+      static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * BS)
     return fail(PKV_ERR_INVALID_ARGUMENT, "max_context_len %d vs max_blocks_per_seq %d",
                 max_context_len, max_blocks_per_seq);
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARGUMENT, "scale is not finite");
-  const bool sk_path = use_stream_k(num_seqs, num_q_heads, cache->num_kv_heads, partition_size);
   const int32_t part = sk_path ? kBlock : resolve_partition(max_context_len, partition_size);
   if (part == 0) return fail(PKV_ERR_INVALID_ARGUMENT, "partition_size %d", partition_size);
   if (num_seqs == 0) return PKV_OK;
@@ -627,7 +638,6 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
   if (append && max_blocks_per_seq == 0)
     return fail(PKV_ERR_INVALID_ARGUMENT, "an append needs a block table (max_blocks_per_seq > 0)");
   if (sk_path) {
-    if (cache->dtype == PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "group size %d needs f16/bf16", G);
     const size_t need = sk::sk_workspace_bytes(num_seqs, cache->num_kv_heads, D, max_context_len);
     if (!workspace || workspace_bytes < need)
       return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", need, workspace ? workspace_bytes : 0);
@@ -649,6 +659,7 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
     sp.max_blocks_per_seq = max_blocks_per_seq;
     sp.max_context_len = max_context_len;
     sp.num_blocks = cache->num_blocks;
+    sp.block_size = BS;
     sp.ranges = sk::sk_ranges(num_seqs, cache->num_kv_heads, max_context_len);
     sp.scale_log2e = scale * kLog2e;
     const int64_t recs = static_cast<int64_t>(sp.ranges) * sp.num_kv_heads * 2;
@@ -663,7 +674,7 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
   if (num_seqs > 65535 || P > 65535)
     return fail(PKV_ERR_UNSUPPORTED, "grid too large (num_seqs %d, partitions %d)", num_seqs, P);
   const size_t need = pkv_paged_attn_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads, D,
-                                                     max_context_len, partition_size);
+                                                     max_context_len, partition_size, cache->dtype);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", need, workspace ? workspace_bytes : 0);
   if (need > 0 && !aligned16(workspace))

@@ -45,7 +45,7 @@ namespace pkv {
 namespace sk {
 namespace {
 
-constexpr int kBlock = 16;
+constexpr int kTile = 16;                 // tokens per tile (one MFMA row block)
 // Work-group shape: kHeads KV heads side by side (their waves read neighbouring slices of the
 // same token rows together) x kSplits consecutive sub-ranges of the tile list (merged in LDS).
 constexpr int kHeads = 4;
@@ -54,7 +54,9 @@ constexpr int kWaves = kHeads * kSplits;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kNegBig = -1.0e30f;
 constexpr float kTau = 8.0f;              // lazy-rescale threshold (log2 units)
-constexpr int kLast = 1 << 8;             // tile flag: last block of its sequence
+constexpr int kLast = 1 << 8;             // tile flag: last tile of its sequence
+constexpr int kFirst = 1 << 9;            // tile flag: first tile of its sequence
+constexpr int kHalf = 1 << 10;            // tile flag (32-token blocks): second half of its block
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // buffer descriptor dword 3 for gfx9-class parts
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -153,7 +155,11 @@ __device__ __forceinline__ void store_rows(typename T::raw* o, const f32x4* v, f
   wave_lds_sync();
 }
 
-// Per-lane tile entry of tile t (t < T): {physical block, sequence, block index, ntok | kLast}.
+// Per-lane tile entry of tile t (t < T): {block of rows 0-15 (8-token blocks: rows 0-7),
+// sequence, block of rows 8-15 (8-token blocks only, else -1), ntok | flags}.  A tile is 16
+// tokens of one sequence: for 16-token pool blocks one block, for 32-token blocks one half of
+// a block (kHalf: the second half), for 8-token blocks two blocks.
+template <int BS>
 __device__ __forceinline__ int4 tile_entry(const SkParams& p, const int* s_cu, int t) {
   int a = 0, b = p.num_seqs;  // largest a with cu[a] <= t  (cu[0] = 0 <= t < cu[B] = T)
   while (b - a > 1) {
@@ -161,15 +167,28 @@ __device__ __forceinline__ int4 tile_entry(const SkParams& p, const int* s_cu, i
     if (s_cu[m] <= t) a = m; else b = m;
   }
   const int j = t - s_cu[a];
-  const int nblk = s_cu[a + 1] - s_cu[a];
+  const int ntiles = s_cu[a + 1] - s_cu[a];
   const int L = clamp_ctx(p.context_lens[a], p.max_context_len);
-  // The table entry is read whatever the length, so that both loads are in flight together
-  // (j is below max_blocks_per_seq whenever that is positive).  The empty tile of a sequence
-  // with no context reads nothing (block id -1) and has 0 tokens.
-  const int entry = p.max_blocks_per_seq > 0 ? p.block_tables[static_cast<int64_t>(a) * p.max_blocks_per_seq + j] : -1;
-  const int phys = L > 0 ? entry : -1;
-  const int ntok = min(kBlock, L - j * kBlock);
-  return make_int4(phys, a, j, ntok | (j == nblk - 1 ? kLast : 0));
+  // The table entries are read whatever the length, so that these loads are in flight
+  // together (the indexes stay below max_blocks_per_seq whenever that is positive).  The empty
+  // tile of a sequence with no context reads nothing (block id -1) and has 0 tokens.
+  const int64_t row = static_cast<int64_t>(a) * p.max_blocks_per_seq;
+  int e0 = -1, e1 = -1;
+  if (p.max_blocks_per_seq > 0) {
+    if (BS == 16) {
+      e0 = p.block_tables[row + j];
+    } else if (BS == 32) {
+      e0 = p.block_tables[row + (j >> 1)];
+    } else {
+      e0 = p.block_tables[row + 2 * j];
+      if (2 * j + 1 < p.max_blocks_per_seq) e1 = p.block_tables[row + 2 * j + 1];
+    }
+  }
+  const int ntok = min(kTile, L - j * kTile);
+  const int phys0 = L > 0 ? e0 : -1;
+  const int phys1 = (BS == 8 && ntok > 8) ? e1 : -1;
+  const int fl = ntok | (j == ntiles - 1 ? kLast : 0) | (j == 0 ? kFirst : 0) | ((BS == 32 && (j & 1)) ? kHalf : 0);
+  return make_int4(phys0, a, phys1, fl);
 }
 
 // LDS layout of the decode kernel (dynamic): the prefix sum of block counts, then one region
@@ -178,12 +197,12 @@ __host__ __device__ constexpr int sk_pitch(int D) { return D == 128 ? 288 : 160;
 __host__ __device__ inline int sk_state_bytes(int D, int G) { return ((D / 16) * 4 * G * 16 + G * 8 + 15) / 16 * 16; }
 __host__ __device__ inline int sk_cu_bytes(int B) { return ((B + 1) * 4 + 15) / 16 * 16; }
 __host__ __device__ inline int sk_lds_bytes(int B, int D, int G) {
-  const int tiles = kWaves * kBlock * sk_pitch(D);
+  const int tiles = kWaves * kTile * sk_pitch(D);
   const int states = 2 * kWaves * sk_state_bytes(D, G);
   return sk_cu_bytes(B) + (tiles > states ? tiles : states);
 }
 
-template <typename T, int D>
+template <typename T, int D, int BS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_sk_kernel(SkParams p) {
   using M = Mma<T>;
@@ -192,7 +211,7 @@ void decode_sk_kernel(SkParams p) {
   constexpr int KC = D / 32;                   // QK k-chunks (one 16-byte piece per lane each)
   constexpr int NC = D / 16;                   // PV output chunks of 16 columns
   constexpr int PITCH = sk_pitch(D);           // V tile row pitch: the transposing reads hit distinct banks
-  constexpr int TILE_LDS = kBlock * PITCH;
+  constexpr int TILE_LDS = kTile * PITCH;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -219,7 +238,7 @@ void decode_sk_kernel(SkParams p) {
   const int lo = min(B, tid * per), hi = min(B, lo + per);
   int run = 0;
   for (int s = lo; s < hi; ++s) {
-    run += max(1, (clamp_ctx(p.context_lens[s], p.max_context_len) + kBlock - 1) / kBlock);
+    run += max(1, (clamp_ctx(p.context_lens[s], p.max_context_len) + kTile - 1) / kTile);
     s_cu[s + 1] = run;
   }
   // exclusive offset of this thread's sequences: a scan within the wave, then over the waves
@@ -275,11 +294,12 @@ void decode_sk_kernel(SkParams p) {
   if (n > 0) {
     // tile entries: lane i of ent holds tile t0 + kb + i, ent2 the next 64
     int kb = 0;
-    int4 ent = lane < n ? tile_entry(p, s_cu, t0 + lane) : make_int4(0, 0, 0, 0);
+    int4 ent = lane < n ? tile_entry<BS>(p, s_cu, t0 + lane) : make_int4(0, 0, 0, 0);
     int4 ent2;  // read once the first tile's loads are out
 
-    const int64_t block_bytes = static_cast<int64_t>(kBlock) * p.num_kv_heads * ROW;
-    const int voff = r16 * p.num_kv_heads * ROW + g * ROW + grp * 16;
+    const int64_t tok_bytes = static_cast<int64_t>(p.num_kv_heads) * ROW;  // one token row, all heads
+    const int64_t block_bytes = BS * tok_bytes;
+    const int voff = r16 * static_cast<int>(tok_bytes) + g * ROW + grp * 16;
     unsigned char* kbase = static_cast<unsigned char*>(p.k_cache);
     unsigned char* vbase = static_cast<unsigned char*>(p.v_cache);
     unsigned char* vt = s_work + wave * TILE_LDS;
@@ -290,11 +310,15 @@ void decode_sk_kernel(SkParams p) {
     // Issues the loads of tile kk (a zero-length load when kk is past the range or its block
     // id is outside the pool).  A tile that opens a sequence also brings that sequence's
     // query; with a fused append, the last tile of a sequence also brings its new K/V row.
+    // The buffer resource starts at the tile's first row: rows r16 are read at r16 * tok_bytes.
+    // With 8-token blocks rows 8-15 come from a second block, through a second resource whose
+    // base sits 8 rows before that block.
     auto issue = [&](int kk) {
-      int phys = 0, nrec = 0;
+      int phys = 0, nrec = 0, phys1 = 0, nrec1 = 0, half = 0;
       if (kk < n) {
         const int i = kk - kb;
         phys = i < 64 ? lane_val(ent.x, i) : lane_val(ent2.x, i - 64);
+        if (BS == 8) phys1 = i < 64 ? lane_val(ent.z, i) : lane_val(ent2.z, i - 64);
         const int s = i < 64 ? lane_val(ent.y, i) : lane_val(ent2.y, i - 64);
         const int fl = i < 64 ? lane_val(ent.w, i) : lane_val(ent2.w, i - 64);
         if (s != last_s) {
@@ -312,20 +336,37 @@ void decode_sk_kernel(SkParams p) {
 #pragma unroll
           for (int c = 0; c < KC; ++c) { nk[c] = kn[grp + 4 * c]; nv[c] = vn[grp + 4 * c]; }
         }
-        nrec = (phys >= 0 && phys < p.num_blocks) ? static_cast<int>(block_bytes) : 0;
+        nrec = (phys >= 0 && phys < p.num_blocks) ? static_cast<int>((BS == 8 ? 8 : kTile) * tok_bytes) : 0;
         phys = nrec ? phys : 0;
+        if (BS == 32) half = (fl & kHalf) ? 1 : 0;
+        if (BS == 8) {
+          nrec1 = (phys1 >= 0 && phys1 < p.num_blocks) ? static_cast<int>(kTile * tok_bytes) : 0;
+          phys1 = nrec1 ? phys1 : 0;
+        }
       }
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(kbase + phys * block_bytes, 0, nrec, kRsrcWord3);
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(vbase + phys * block_bytes, 0, nrec, kRsrcWord3);
+      const int64_t off = phys * block_bytes + half * kTile * tok_bytes;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(kbase + off, 0, nrec, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(vbase + off, 0, nrec, kRsrcWord3);
+      if (BS != 8 || r16 < 8) {
 #pragma unroll
-      for (int c = 0; c < KC; ++c) kbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff + c * 64, 0, 0);
+        for (int c = 0; c < KC; ++c) kbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff + c * 64, 0, 0);
 #pragma unroll
-      for (int c = 0; c < KC; ++c) vbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + c * 64, 0, 0);
+        for (int c = 0; c < KC; ++c) vbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + c * 64, 0, 0);
+      } else {
+        const int64_t off1 = phys1 * block_bytes - 8 * tok_bytes;
+        const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc(kbase + off1, 0, nrec1, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rv1 = __builtin_amdgcn_make_buffer_rsrc(vbase + off1, 0, nrec1, kRsrcWord3);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) kbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rk1, voff + c * 64, 0, 0);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) vbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rv1, voff + c * 64, 0, 0);
+      }
     };
     issue(0);
-    ent2 = lane + 64 < n ? tile_entry(p, s_cu, t0 + 64 + lane) : make_int4(0, 0, 0, 0);
+    ent2 = lane + 64 < n ? tile_entry<BS>(p, s_cu, t0 + 64 + lane) : make_int4(0, 0, 0, 0);
 
-    int cur_s = -1, seg_j0 = 0, seg_k0 = 0;
+    int cur_s = -1, seg_k0 = 0;
+    bool seg_first = false;  // the current segment starts at its sequence's first tile
     typename M::v8 qb[KC];
     // transposing read of PV chunk c: row 4*grp + (r16 >> 2), columns 16c + 4*(r16 & 3) .. +3
     const int tr_base = (4 * grp + (r16 >> 2)) * PITCH + 8 * (r16 & 3);
@@ -334,14 +375,14 @@ void decode_sk_kernel(SkParams p) {
       if (k - kb == 64) {  // slide the entry window
         kb += 64;
         ent = ent2;
-        ent2 = kb + 64 + lane < n ? tile_entry(p, s_cu, t0 + kb + 64 + lane) : make_int4(0, 0, 0, 0);
+        ent2 = kb + 64 + lane < n ? tile_entry<BS>(p, s_cu, t0 + kb + 64 + lane) : make_int4(0, 0, 0, 0);
       }
       const int i = k - kb;
-      const int s = lane_val(ent.y, i), j = lane_val(ent.z, i), fl = lane_val(ent.w, i);
+      const int s = lane_val(ent.y, i), fl = lane_val(ent.w, i);
       const int ntok = fl & 0xff;
       if (s != cur_s) {  // this tile opens a segment
         cur_s = s;
-        seg_j0 = j;
+        seg_first = (fl & kFirst) != 0;
         seg_k0 = k;
 #pragma unroll
         for (int c = 0; c < KC; ++c) qb[c] = __builtin_bit_cast(typename M::v8, r16 < G ? qbuf[c] : u32x4{0u, 0u, 0u, 0u});
@@ -394,7 +435,7 @@ void decode_sk_kernel(SkParams p) {
       }
       l_run += psum;
       wave_lds_sync();
-      if (ntok < kBlock) {  // last block of a sequence: rows past the context may hold anything
+      if (ntok < kTile) {  // last tile of a sequence: rows past the context may hold anything
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + tr_base + 32 * c));
@@ -418,11 +459,11 @@ void decode_sk_kernel(SkParams p) {
       }
       if (!seg_end) continue;
       const float lsum = swap32_sum(swap16_sum(l_run));
-      if (seg_j0 == 0 && (fl & kLast)) {  // the whole sequence lies in this wave's sub-range
+      if (seg_first && (fl & kLast)) {  // the whole sequence lies in this wave's sub-range
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
         store_rows<T, D>(static_cast<raw*>(p.out) + (static_cast<int64_t>(s) * p.num_q_heads + g * G) * D, acc, inv,
                          vt, G, lane);
-      } else if (seg_k0 == 0 && seg_j0 > 0) {  // began in an earlier sub-range (A)
+      } else if (seg_k0 == 0 && !seg_first) {  // began in an earlier sub-range (A)
         hasA = true;
         a_through = !(fl & kLast);
         sA = s;
@@ -652,10 +693,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
       if (gg >= p.num_kv_heads) continue;
       const int L = clamp_ctx(p.context_lens[s], p.max_context_len);
       if (L == 0) continue;
-      const int phys = p.block_tables[static_cast<int64_t>(s) * p.max_blocks_per_seq + (L - 1) / kBlock];
+      const int phys = p.block_tables[static_cast<int64_t>(s) * p.max_blocks_per_seq + (L - 1) / p.block_size];
       if (phys < 0 || phys >= p.num_blocks) continue;
       const int64_t src = (static_cast<int64_t>(s) * p.num_kv_heads + gg) * row_bytes + ch;
-      const int64_t dst = ((static_cast<int64_t>(phys) * kBlock + (L - 1) % kBlock) * p.num_kv_heads + gg) * row_bytes + ch;
+      const int64_t dst = ((static_cast<int64_t>(phys) * p.block_size + (L - 1) % p.block_size) * p.num_kv_heads + gg) *
+                              row_bytes + ch;
       const u32x4 kr = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(p.new_key) + src);
       const u32x4 vr = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(p.new_value) + src);
       *reinterpret_cast<u32x4*>(static_cast<unsigned char*>(p.k_cache) + dst) = kr;
@@ -664,11 +706,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int BS>
 hipError_t launch(const SkParams& p, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(sk_lds_bytes(p.num_seqs, D, p.group));
   const int hgroups = (p.num_kv_heads + kHeads - 1) / kHeads;
-  hipLaunchKernelGGL((decode_sk_kernel<T, D>), dim3(p.ranges * hgroups), dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL((decode_sk_kernel<T, D, BS>), dim3(p.ranges * hgroups), dim3(kThreads), lds, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((merge_sk_kernel<T, D>), dim3(p.ranges * hgroups), dim3(kMergeThreads),
@@ -676,12 +718,19 @@ hipError_t launch(const SkParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename T, int D>
+hipError_t launch_bs(const SkParams& p, hipStream_t stream) {
+  if (p.block_size == 8) return launch<T, D, 8>(p, stream);
+  if (p.block_size == 32) return launch<T, D, 32>(p, stream);
+  return launch<T, D, 16>(p, stream);
+}
+
 }  // namespace
 
 int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
   // About 8 waves per CU on a 256-CU part (one work-group of 8 waves per range and group of 4
   // KV heads), and at least 32 tiles per range in the worst case.
-  const int64_t max_blocks = (static_cast<int64_t>(max_context_len) + kBlock - 1) / kBlock;
+  const int64_t max_blocks = (static_cast<int64_t>(max_context_len) + kTile - 1) / kTile;
   const int64_t upper_tiles = static_cast<int64_t>(num_seqs) * max_blocks;
   const int64_t hgroups = (num_kv_heads + kHeads - 1) / kHeads;
   int64_t r = kSkTargetWaves / (hgroups * kWaves);
@@ -706,8 +755,8 @@ size_t sk_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_d
 
 hipError_t sk_launch(SkParams p, int32_t dtype, hipStream_t stream) {
   const int D = p.head_dim;
-  if (dtype == PKV_BF16) return D == 64 ? launch<BF16, 64>(p, stream) : launch<BF16, 128>(p, stream);
-  return D == 64 ? launch<F16, 64>(p, stream) : launch<F16, 128>(p, stream);
+  if (dtype == PKV_BF16) return D == 64 ? launch_bs<BF16, 64>(p, stream) : launch_bs<BF16, 128>(p, stream);
+  return D == 64 ? launch_bs<F16, 64>(p, stream) : launch_bs<F16, 128>(p, stream);
 }
 
 }  // namespace sk

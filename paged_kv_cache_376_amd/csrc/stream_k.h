@@ -35,6 +35,7 @@ struct SkParams {
   int32_t max_blocks_per_seq;
   int32_t max_context_len;
   int32_t num_blocks;
+  int32_t block_size;  // tokens per pool block: 8, 16 or 32 (a tile is always 16 tokens)
   int32_t ranges;  // equal tile ranges per KV head (one work-group of 4 waves each)
   float scale_log2e;
 };

@@ -281,13 +281,16 @@ def test_workspace_size_and_partition_rules():
     assert ps(8, 32, 8, 128, 32768, 1024) == 1024
     assert ps(8, 32, 8, 128, 32768, 24) == 0
     assert ws(8, 32, 8, 128, 32768, 1024) == 8 * 32 * 32 * 130 * 4
-    # auto with G <= 2: fixed partitions of an automatic size
-    auto = ps(64, 32, 32, 128, 8192, 0)
+    # auto with f32 pools: fixed partitions of an automatic size
+    auto = ps(64, 32, 32, 128, 8192, 0, "float32")
     assert auto % 16 == 0 and auto > 0
     P = -(-8192 // auto)
-    assert ws(64, 32, 32, 128, 8192, 0) == (0 if P == 1 else 64 * 32 * P * 130 * 4)
-    assert ws(4, 4, 4, 64, 100, 0) == 0
-    # auto with G > 2: the even split over the GPU has no fixed partition; its workspace
+    assert ws(64, 32, 32, 128, 8192, 0, "float32") == (0 if P == 1 else 64 * 32 * P * 130 * 4)
+    assert ws(4, 4, 4, 64, 100, 0, "float32") == 0
+    # auto with 16-bit pools takes the even split whatever the group size
+    assert ps(64, 32, 32, 128, 8192, 0, "float16") == 0 and ws(64, 32, 32, 128, 8192, 0, "float16") > 0
+    assert ws(64, 32, 32, 128, 8192, 0, 7) == 0 and ps(64, 32, 32, 128, 8192, 0, 7) == 0  # unknown dtype
+    # auto with 16-bit pools: the even split over the GPU has no fixed partition; its workspace
     # holds, per work range, records (16 x D fp32 acc + 16 x 2 stats, two per KV head) and
     # one 16-byte descriptor
     assert ps(256, 64, 8, 128, 8192, 0) == 0

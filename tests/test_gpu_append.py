@@ -84,7 +84,7 @@ def test_decode_step_append_full_size(name):
 
 
 FUSED = [
-    # (spec overrides, partition): even split (G > 2), fixed partitions, MHA, fp32
+    # (spec overrides, partition): even split (GQA, MHA), fixed partitions, fp32
     (W.SPECS["gqa_bf16"].replace(num_seqs=10, len_hi=900), 0),
     (W.SPECS["gqa_bf16"].replace(num_seqs=10, len_hi=900), 64),
     (W.Spec("f16g4d64", "float16", 6, 16, 4, 64, "fixed", fixed_lengths=(15, 16, 31, 200, 1, 600)), 0),

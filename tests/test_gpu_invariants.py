@@ -1,5 +1,7 @@
 """GPU invariants of paged decode: properties fixed by the definition, checked bit for bit
-where rounding cannot enter, on both kernel variants (VALU: G <= 2, MFMA: G > 2)."""
+where rounding cannot enter, on every kernel variant: the even split over the GPU (partition
+0 with f16/bf16 pools, any group size) and fixed partitions (VALU for f32 and G <= 2, MFMA for
+G > 2)."""
 
 import numpy as np
 import pytest
@@ -115,10 +117,10 @@ def test_shared_prefix_and_copy_give_identical_outputs(variant):
     for partition in (0, 64):
         out = decode(cache, q, bt, ctx, maxc, 1.0 / np.sqrt(d), partition)
         # Fixed partitions treat every sequence alike, so equal inputs give equal bits.  The
-        # even split over the GPU (partition 0 with G > 2) cuts each sequence where the range
-        # boundaries happen to fall, so equal sequences at different batch positions may be
-        # merged in a different grouping: equal up to rounding.
-        exact = partition != 0 or hq // hkv <= 2
+        # even split over the GPU (partition 0 with f16/bf16 pools) cuts each sequence where
+        # the range boundaries happen to fall, so equal sequences at different batch positions
+        # may be merged in a different grouping: equal up to rounding.
+        exact = partition != 0 or dtype == "float32"
         for s in range(1, 5):
             if exact:
                 assert torch.equal(bits(out[s]), bits(out[0])), s
@@ -175,7 +177,7 @@ def test_nan_canaries_beyond_the_context_are_never_read(variant):
 
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("bfloat16", 16, 2, 128), ("float16", 12, 3, 64), ("bfloat16", 40, 5, 128)])
 def test_even_split_edge_cases(dtype, hq, hkv, d):
-    """The even split over the GPU (partition 0, G > 2): every context empty gives zeros; one
+    """The even split over the GPU (partition 0, f16/bf16): every context empty gives zeros; one
     long sequence cut into many ranges, empty sequences between others, and a KV-head count
     that is not a multiple of the work-group's 4 heads all match the oracle."""
     say(f"[split edges] {dtype} Hq={hq} Hkv={hkv} D={d}")
