@@ -270,6 +270,9 @@ def main():
                     help="step: the decode step (default); copy_blocks: pkv_copy_blocks "
                          "(copy-on-write) GB/s; swap: pkv_swap_blocks device<->pinned host GB/s; "
                          "append: pkv_kv_cache_append of a prefill chunk GB/s")
+    ap.add_argument("--prefix-shared", action="store_true",
+                    help="decode with pkv_paged_attn_decode_prefix (groups from pkv_pool_prefix_groups), "
+                         "after a separate append")
     ap.add_argument("--block-size", type=int, default=0,
                     help="tokens per pool block (default: the workload's, 16)")
     ap.add_argument("--append-tokens", type=int, default=16384,
@@ -333,13 +336,28 @@ def main():
         binding.paged_attn_decode(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale,
                                   workspace=ws, partition_size=args.partition, stream=stream)
 
+    if args.prefix_shared:
+        sp_, offs_, mem_, mx_ = cache.pool.prefix_groups(seqs)
+        to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+        sp_d, offs_d, mem_d = to_dev(sp_), to_dev(offs_), to_dev(mem_)
+        pws = binding.paged_attn_decode_prefix_workspace_bytes(sp.num_seqs, sp.num_q_heads, sp.num_kv_heads,
+                                                               sp.head_dim, maxc, mx_, sp.dtype)
+        pws_t = torch.empty(max(pws, 16), dtype=torch.uint8, device=dev)
+        log(f"prefix groups: {len(offs_) - 1}, longest shared prefix {mx_} tokens")
+
+    def prefix_call():
+        binding.paged_attn_decode_prefix(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale, sp_d, offs_d,
+                                         mem_d, mx_, workspace=pws_t, stream=stream)
+
     def fused_call():
         binding.paged_attn_decode_append(out, q, new_k, new_v, cache.k_cache, cache.v_cache, bt, ctx,
                                          maxc, w.scale, workspace=ws, partition_size=args.partition,
                                          stream=stream)
 
-    calls = [append_call, decode_call] if args.separate else [fused_call]
-    log(f"warmup {args.warmup} steps ({'append + decode' if args.separate else 'fused append+decode'}, "
+    calls = ([append_call, prefix_call] if args.prefix_shared else
+             [append_call, decode_call] if args.separate else [fused_call])
+    two_calls = args.separate or args.prefix_shared
+    log(f"warmup {args.warmup} steps ({'append + decode' if two_calls else 'fused append+decode'}, "
         f"partition {part or 'even split'}, workspace {ws_bytes} B)")
     for _ in range(args.warmup):
         for c in calls:
@@ -371,8 +389,8 @@ def main():
     torch.cuda.synchronize()
     t_calls = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(len(calls))] for i in range(K)])
     t_dec = t_calls[:, -1]
-    t_app = t_calls[:, 0] if args.separate else None
-    if args.separate:
+    t_app = t_calls[:, 0] if two_calls else None
+    if two_calls:
         log(f"step {ms_step * 1e3:.1f} us: append {t_app.mean() * 1e3:.1f} us, decode "
             f"median {np.median(t_dec) * 1e3:.1f} us (p10 {np.percentile(t_dec, 10) * 1e3:.1f}, "
             f"p90 {np.percentile(t_dec, 90) * 1e3:.1f})")
@@ -383,7 +401,7 @@ def main():
     kv_bytes, dec_bytes = algorithmic_bytes(w)
     e_bytes = {"float32": 4, "float16": 2, "bfloat16": 2}[sp.dtype]
     app_bytes = 4 * sp.num_seqs * sp.num_kv_heads * sp.head_dim * e_bytes  # new rows read + written
-    if not args.separate:
+    if not two_calls:
         dec_bytes += app_bytes
     dec_s = float(t_dec.mean()) / 1e3
     gbs = kv_bytes / (ms_step / 1e3) / 1e9
@@ -416,7 +434,8 @@ def main():
         "decode_tokens_per_s_70b_shape_attention_only": round(sp.num_seqs / (LAYERS_70B * ms_step / 1e3), 1),
         "append_us": None if t_app is None else round(float(t_app.mean()) * 1e3, 2),
         "decode_us_median": round(float(np.median(t_dec)) * 1e3, 2),
-        "step_calls": "pkv_kv_cache_append + pkv_paged_attn_decode" if args.separate
+        "step_calls": "pkv_kv_cache_append + pkv_paged_attn_decode_prefix" if args.prefix_shared
+                      else "pkv_kv_cache_append + pkv_paged_attn_decode" if args.separate
                       else "pkv_paged_attn_decode_append (append fused into the decode)",
         "config": {
             "workload": f"{sp.name}: paged decode, B={sp.num_seqs}, Hq={sp.num_q_heads}, "
@@ -429,7 +448,8 @@ def main():
             "pool_blocks": w.num_blocks,
         },
         "roofline": {
-            "kernel": ("pkv_paged_attn_decode" if args.separate else "pkv_paged_attn_decode_append") +
+            "kernel": ("pkv_paged_attn_decode_prefix" if args.prefix_shared else
+                       "pkv_paged_attn_decode" if args.separate else "pkv_paged_attn_decode_append") +
                       " (decode kernel + merge of sequences cut by the split)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -437,7 +457,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             # counters were taken on the default workload with the fused call
-            "traffic": counter_traffic() if (args.config == "gqa_bf16" and args.seed == 0 and not args.separate
+            "traffic": counter_traffic() if (args.config == "gqa_bf16" and args.seed == 0 and not two_calls
                                              and args.partition == 0) else None,
             "bytes_per_launch": dec_bytes,
             "avg_launch_us": round(dec_s * 1e6, 2),

@@ -220,6 +220,54 @@ PKV_API pkv_status pkv_paged_attn_decode_append(void* out, const void* q,
                                         void* workspace, size_t workspace_bytes,
                                         int32_t partition_size, void* stream);
 
+/* Decode attention with prefix sharing: the same result as pkv_paged_attn_decode (up to
+ * rounding), computed so that a prefix shared by a group of sequences is read once per group.
+ *
+ * Sequences that share the physical blocks of the start of their contexts (prefix sharing by
+ * reference to the same blocks, [yunthe] section "PagedAttention分页注意力机制原理"; one block
+ * shared by several requests, [111cn] §3.2) attend over that shared prefix in one pass for
+ * the whole group: a work-group takes 16 prefix tiles of one KV head and its waves take the
+ * group's query rows (member x query head), so every prefix tile is read once for the group.
+ * Each sequence's own remainder is attended by the even split over the GPU, and the two parts
+ * are merged exactly with the log-sum-exp rule (fixed order: deterministic).
+ *
+ * Arguments as for pkv_paged_attn_decode (f16/bf16 pools, block size 8, 16 or 32, at most 8192
+ * sequences; no partition_size), plus the group description that pkv_pool_prefix_groups
+ * produces, copied to device memory:
+ *   seq_prefix     device int32 [num_seqs]: shared prefix tokens of each sequence, a multiple
+ *                  of 16, 0 for sequences in no group
+ *   group_offsets  device int32 [num_groups + 1]: group i is group_members[offsets[i] ..
+ *                  offsets[i+1])
+ *   group_members  device int32: batch positions (0 .. num_seqs-1)
+ *   num_groups     >= 0
+ *   max_prefix_tokens  host int: >= every seq_prefix, a multiple of 16, <= max_context_len
+ *   workspace      >= pkv_paged_attn_decode_prefix_workspace_bytes(...) bytes
+ * Device-side contract: the members of a group have the same seq_prefix P <= their context
+ * lengths, and the first P tokens of their tables name the same blocks (the kernels read a
+ * group's prefix through its first member's table); sequences in no group have 0.
+ * Errors: as pkv_paged_attn_decode; UNSUPPORTED for f32 pools or more than 8192 sequences;
+ * INVALID_ARGUMENT for a bad group description (null pointers, num_groups < 0, bad
+ * max_prefix_tokens). */
+PKV_API pkv_status pkv_paged_attn_decode_prefix(void* out, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        const pkv_cache_desc* cache,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t max_context_len,
+                                        int32_t num_seqs, int32_t num_q_heads, float scale,
+                                        const int32_t* seq_prefix, const int32_t* group_offsets,
+                                        const int32_t* group_members, int32_t num_groups,
+                                        int32_t max_prefix_tokens, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pkv_paged_attn_decode_prefix needs (the even split's, plus fp32
+ * suffix results [num_seqs][num_q_heads][head_dim + 1] and prefix partials
+ * [num_seqs][num_q_heads][ceil(max_prefix_tokens / 256)][head_dim + 2], each region rounded up
+ * to 256 bytes).  0 for arguments the call would reject. */
+PKV_API size_t pkv_paged_attn_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                    int32_t num_kv_heads, int32_t head_dim,
+                                                    int32_t max_context_len,
+                                                    int32_t max_prefix_tokens, int32_t dtype);
+
 /* ------------------------------------------------------------------------------------ */
 /* Device: whole-block copies (copy-on-write, swap)                                      */
 /* ------------------------------------------------------------------------------------ */
@@ -330,6 +378,23 @@ PKV_API pkv_status pkv_seq_free(pkv_block_pool* pool, int64_t seq);
 
 /* Token count of seq, or -1 if unknown. */
 PKV_API int64_t pkv_seq_context_len(const pkv_block_pool* pool, int64_t seq);
+
+/* Finds groups of batch entries whose contexts start with the same physical blocks, for
+ * pkv_paged_attn_decode_prefix.  Entries (seqs[0..n-1], batch positions 0..n-1) are bucketed by
+ * their first block; a bucket of two or more entries shares the leading table entries common to
+ * all its members, counting only blocks every member fills completely; its prefix is that many
+ * tokens rounded down to a multiple of 16.  A bucket whose prefix is below max(16,
+ * min_prefix_tokens) is not a group.  Groups are listed in order of their first member, members
+ * in batch order.
+ *   seq_prefix_out     int32 [n]: the entry's group prefix in tokens, or 0
+ *   group_offsets_out  int32 [n + 1]: group i is group_members_out[offsets[i] .. offsets[i+1])
+ *   group_members_out  int32 [n]: batch positions
+ *   num_groups_out, max_prefix_out: number of groups, longest prefix (0 if none)
+ * Errors: INVALID_ARGUMENT (null pool or output, n < 0, min_prefix_tokens < 0), NOT_FOUND. */
+PKV_API pkv_status pkv_pool_prefix_groups(const pkv_block_pool* pool, const int64_t* seqs, int32_t n,
+                                  int32_t min_prefix_tokens, int32_t* seq_prefix_out,
+                                  int32_t* group_offsets_out, int32_t* group_members_out,
+                                  int32_t* num_groups_out, int32_t* max_prefix_out);
 
 /* Moves whole sequences from pool `src` to pool `dst` (for example from the device pool to a
  * pool in pinned host memory and back): the swap space of [yunthe] section "生产部署注意事项",

@@ -213,6 +213,46 @@ class BlockManager:
             self.free(s)
         return [(b, new_id[b]) for b in first_use]
 
+    def prefix_groups(self, seqs, min_prefix_tokens: int = 0):
+        """Groups of batch entries whose contexts start with the same physical blocks.
+
+        Prefix sharing is sharing by reference: sequences point at the same physical blocks
+        for their common start (yunthe.com page, section "PagedAttention分页注意力机制原理";
+        111cn.net page §3.2, one physical block shared by several requests).  A shared prefix
+        is read off the tables as follows:
+
+        1. batch entries with at least one full block are bucketed by their first block id;
+        2. in a bucket of two or more, the prefix is the run of leading table entries equal for
+           every member, counting only blocks every member fills completely;
+        3. its length in tokens is rounded down to a multiple of 16 (whole 16-token tiles);
+        4. a bucket whose prefix is below max(16, min_prefix_tokens) is not a group.
+
+        Returns (seq_prefix per entry, groups as lists of batch positions in batch order, the
+        groups ordered by their first member)."""
+        seqs = [int(x) for x in seqs]
+        bs = self.block_size
+        seq_prefix = [0] * len(seqs)
+        buckets: dict[int, list[int]] = {}
+        for i, s in enumerate(seqs):
+            if self.num_tokens[s] // bs >= 1:
+                buckets.setdefault(self.block_tables[s][0], []).append(i)
+        groups = []
+        for members in buckets.values():  # insertion order = order of first appearance
+            if len(members) < 2:
+                continue
+            tabs = [self.block_tables[seqs[i]] for i in members]
+            full = min(self.num_tokens[seqs[i]] // bs for i in members)
+            k = 0
+            while k < full and all(t[k] == tabs[0][k] for t in tabs):
+                k += 1
+            tokens = (k * bs) // 16 * 16
+            if tokens < max(16, min_prefix_tokens):
+                continue
+            for i in members:
+                seq_prefix[i] = tokens
+            groups.append(list(members))
+        return seq_prefix, groups
+
     def tables(self, seqs, max_blocks_per_seq: int):
         """Padded table rows (pad -1) and context lengths for ``seqs``, in that order."""
         rows, lens = [], []

@@ -45,6 +45,10 @@ SIGNATURES = {
     "pkv_copy_blocks": (_I32, [_P, _P, _P, _P, _I32, _P]),
     "pkv_swap_blocks": (_I32, [_P, _P, _I32, _P, _P, _I32, _P, _P, _I32, _P]),
     "pkv_pool_move_seqs": (_I32, [_P, _P, _PI64, _I32, _PI32, _I32, _PI32]),
+    "pkv_pool_prefix_groups": (_I32, [_P, _PI64, _I32, _I32, _PI32, _PI32, _PI32, _PI32, _PI32]),
+    "pkv_paged_attn_decode_prefix": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, ctypes.c_float,
+                                            _P, _P, _P, _I32, _I32, _P, ctypes.c_size_t, _P]),
+    "pkv_paged_attn_decode_prefix_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_pool_create": (_I32, [_I32, _I32, _PI32, ctypes.POINTER(_P)]),
     "pkv_pool_destroy": (None, [_P]),
     "pkv_pool_num_blocks": (_I32, [_P]),
@@ -247,6 +251,43 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_
         B, Hq, float(scale), _ptr(workspace), ws_bytes, int(partition_size), _stream(stream)))
 
 
+def paged_attn_decode_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                             max_prefix_tokens, dtype="bfloat16") -> int:
+    return int(lib().pkv_paged_attn_decode_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                                  max_context_len, max_prefix_tokens,
+                                                                  _dtype_code(dtype)))
+
+
+def paged_attn_decode_prefix(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                             seq_prefix, group_offsets, group_members, max_prefix_tokens, workspace=None,
+                             stream=None) -> None:
+    """pkv_paged_attn_decode_prefix: decode with each group's shared prefix read once per group.
+    seq_prefix / group_offsets / group_members: int32 device tensors (pkv_pool_prefix_groups)."""
+    import torch
+
+    _same(out, q, k_cache, v_cache)
+    desc = cache_desc(k_cache)
+    B, Hq, D = q.shape
+    if tuple(out.shape) != (B, Hq, D) or D != desc.head_dim:
+        raise ValueError("q/out must be [B, Hq, D] with the cache's D")
+    for t in (block_tables, context_lens, seq_prefix, group_offsets, group_members):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("tables, lengths and group arrays must be contiguous int32")
+    if seq_prefix.numel() != B or group_offsets.numel() < 1:
+        raise ValueError("seq_prefix must have B entries, group_offsets at least one")
+    ng = group_offsets.numel() - 1
+    need = paged_attn_decode_prefix_workspace_bytes(B, Hq, desc.num_kv_heads, D, max_context_len, max_prefix_tokens,
+                                                    desc.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_paged_attn_decode_prefix(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), int(max_context_len), B, Hq, float(scale), _ptr(seq_prefix),
+        _ptr(group_offsets), _ptr(group_members), ng, int(max_prefix_tokens), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
 def paged_attn_decode_append(out, q, new_key, new_value, k_cache, v_cache, block_tables,
                              context_lens, max_context_len, scale, workspace=None, partition_size=0,
                              stream=None) -> None:
@@ -360,6 +401,20 @@ class BlockPool:
         _check(lib().pkv_pool_move_seqs(self._h, dst._h, s.ctypes.data_as(_PI64), s.size,
                                         pairs.ctypes.data_as(_PI32), cap, ctypes.byref(npairs)))
         return pairs[:npairs.value]
+
+    def prefix_groups(self, seqs, min_prefix_tokens: int = 0):
+        """pkv_pool_prefix_groups: (seq_prefix int32 [n], group_offsets int32 [g+1],
+        group_members int32 [m], max_prefix) for the batch ``seqs``."""
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = s.size
+        sp = np.zeros(max(n, 1), dtype=np.int32)
+        offs = np.zeros(n + 1, dtype=np.int32)
+        mem = np.zeros(max(n, 1), dtype=np.int32)
+        ng, mx = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(lib().pkv_pool_prefix_groups(self._h, s.ctypes.data_as(_PI64), n, min_prefix_tokens,
+                                            sp.ctypes.data_as(_PI32), offs.ctypes.data_as(_PI32),
+                                            mem.ctypes.data_as(_PI32), ctypes.byref(ng), ctypes.byref(mx)))
+        return sp[:n], offs[:ng.value + 1], mem[:offs[ng.value]], int(mx.value)
 
     def seq_context_len(self, seq: int) -> int:
         return int(lib().pkv_seq_context_len(self._h, seq))

@@ -11,6 +11,7 @@
 //
 // Every mutating call first computes how many blocks it needs and fails with
 // PKV_ERR_OUT_OF_BLOCKS before touching anything if the free list is too short.
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <unordered_map>
@@ -289,5 +290,68 @@ extern "C" pkv_status pkv_pool_move_seqs(pkv_block_pool* src, pkv_block_pool* ds
     dst->seqs.emplace(seqs[i], std::move(moved));
   }
   if (num_pairs_out) *num_pairs_out = static_cast<int32_t>(order.size());
+  return PKV_OK;
+}
+
+// Groups of batch entries whose contexts start with the same physical blocks (prefix sharing
+// by reference, the yunthe.com page, section "PagedAttention分页注意力机制原理").  Entries are
+// bucketed by their first block; a bucket of two or more shares its members' common leading
+// table entries, counting only blocks every member fills completely; the shared prefix P is
+// that many tokens rounded down to a multiple of 16.  Buckets with P below max(16,
+// min_prefix_tokens) are not grouped.  Groups come in order of their first member.
+extern "C" pkv_status pkv_pool_prefix_groups(const pkv_block_pool* p, const int64_t* seqs, int32_t n,
+                                             int32_t min_prefix_tokens, int32_t* seq_prefix_out,
+                                             int32_t* group_offsets_out, int32_t* group_members_out,
+                                             int32_t* num_groups_out, int32_t* max_prefix_out) {
+  pkv::clear_error();
+  if (!p) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "pool is NULL");
+  if (n < 0 || (n > 0 && !seqs)) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "n=%d seqs=%p", n, (const void*)seqs);
+  if (min_prefix_tokens < 0) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "min_prefix_tokens=%d", min_prefix_tokens);
+  if (!seq_prefix_out || !group_offsets_out || !group_members_out || !num_groups_out || !max_prefix_out)
+    return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "NULL output");
+  std::vector<const pkv_block_pool::Seq*> rows(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = p->seqs.find(seqs[i]);
+    if (it == p->seqs.end()) return pkv::fail(PKV_ERR_NOT_FOUND, "sequence %lld", (long long)seqs[i]);
+    rows[i] = &it->second;
+  }
+  const int64_t bs = p->block_size;
+  std::unordered_map<int32_t, std::vector<int32_t>> bucket;
+  std::vector<int32_t> first_seen;  // first blocks in order of first appearance
+  for (int32_t i = 0; i < n; ++i) {
+    seq_prefix_out[i] = 0;
+    if (rows[i]->num_tokens / bs < 1) continue;  // no full block
+    const int32_t b0 = rows[i]->table[0];
+    auto& v = bucket[b0];
+    if (v.empty()) first_seen.push_back(b0);
+    v.push_back(i);
+  }
+  int32_t ng = 0, off = 0, maxp = 0;
+  for (int32_t b0 : first_seen) {
+    const std::vector<int32_t>& mem = bucket[b0];
+    if (mem.size() < 2) continue;
+    int64_t K = INT64_MAX;
+    for (int32_t i : mem) K = std::min<int64_t>(K, rows[i]->num_tokens / bs);
+    const std::vector<int32_t>& lead = rows[mem[0]]->table;
+    for (int64_t k = 1; k < K; ++k) {
+      bool same = true;
+      for (int32_t i : mem) same = same && rows[i]->table[k] == lead[k];
+      if (!same) {
+        K = k;
+        break;
+      }
+    }
+    const int64_t P = K * bs / 16 * 16;
+    if (P < std::max<int64_t>(16, min_prefix_tokens) || P > INT32_MAX) continue;
+    group_offsets_out[ng++] = off;
+    for (int32_t i : mem) {
+      group_members_out[off++] = i;
+      seq_prefix_out[i] = static_cast<int32_t>(P);
+    }
+    maxp = std::max<int32_t>(maxp, static_cast<int32_t>(P));
+  }
+  group_offsets_out[ng] = off;
+  *num_groups_out = ng;
+  *max_prefix_out = maxp;
   return PKV_OK;
 }

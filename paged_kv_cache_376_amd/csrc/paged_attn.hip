@@ -589,7 +589,28 @@ extern "C" size_t pkv_paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q
 
 namespace {
 
-// Shared body of the two decode entry points.  With new_key/new_value set, each sequence's
+// Group description of a prefix-shared decode (pkv_paged_attn_decode_prefix).
+struct PrefixArgs {
+  const int32_t* seq_prefix;
+  const int32_t* group_offsets;
+  const int32_t* group_members;
+  int32_t num_groups;
+  int32_t max_prefix_tokens;
+};
+
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+inline int32_t prefix_chunks(int32_t max_prefix_tokens) {
+  const int32_t tiles = (max_prefix_tokens + 15) / 16;
+  return (tiles + sk::kPrefixChunkTiles - 1) / sk::kPrefixChunkTiles;
+}
+// Workspace of the prefix path beyond the even split's: suffix results and lse, prefix partials.
+size_t prefix_extra_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t chunks) {
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads;
+  return align256(rows * head_dim * 4) + align256(rows * 4) + align256(rows * chunks * head_dim * 4) +
+         align256(rows * chunks * 8);
+}
+
+// Shared body of the decode entry points.  With new_key/new_value set, each sequence's
 // last token first gets its new K/V row (inside the decode kernel on the evenly split path,
 // by a separate scatter launch otherwise).
 pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -597,7 +618,7 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
                        int32_t max_blocks_per_seq, const int32_t* context_lens,
                        int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, float scale,
                        void* workspace, size_t workspace_bytes, int32_t partition_size, void* stream,
-                       const void* new_key, const void* new_value) {
+                       const void* new_key, const void* new_value, const PrefixArgs* pre = nullptr) {
   clear_error();
   const bool append = new_key != nullptr || new_value != nullptr;
   if (!cache) return fail(PKV_ERR_INVALID_ARGUMENT, "cache descriptor is NULL");
@@ -616,6 +637,12 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
   if (cache->dtype == PKV_F32 ? G > 2 : G > 16)
     return fail(PKV_ERR_UNSUPPORTED, "group size %d for dtype %d (f32: <= 2, f16/bf16: <= 16)", G, cache->dtype);
   const bool sk_path = use_stream_k(num_seqs, num_q_heads, cache->num_kv_heads, partition_size, cache->dtype);
+  if (pre && !sk_path)
+    return fail(PKV_ERR_UNSUPPORTED, "prefix-shared decode needs f16/bf16 pools and at most %d sequences", sk::kSkMaxSeqs);
+  if (pre && (pre->num_groups < 0 || pre->max_prefix_tokens < 0 || pre->max_prefix_tokens % 16 != 0 ||
+              pre->max_prefix_tokens > max_context_len))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "num_groups %d, max_prefix_tokens %d (a multiple of 16, <= max_context_len)",
+                pre ? pre->num_groups : 0, pre ? pre->max_prefix_tokens : 0);
   const int BS = cache->block_size;
   if (sk_path ? (BS != 8 && BS != 16 && BS != 32) : BS != kBlock)
     return fail(PKV_ERR_UNSUPPORTED, "block_size %d (implemented: 8, 16, 32 for f16/bf16 with partition_size 0; "
@@ -637,12 +664,16 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
     return fail(PKV_ERR_INVALID_ARGUMENT, "new_key and new_value must both be 16-byte aligned device pointers");
   if (append && max_blocks_per_seq == 0)
     return fail(PKV_ERR_INVALID_ARGUMENT, "an append needs a block table (max_blocks_per_seq > 0)");
+  if (pre && (!pre->seq_prefix || (pre->num_groups > 0 && (!pre->group_offsets || !pre->group_members))))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "NULL group description");
   if (sk_path) {
-    const size_t need = sk::sk_workspace_bytes(num_seqs, cache->num_kv_heads, D, max_context_len);
+    const size_t sk_bytes = sk::sk_workspace_bytes(num_seqs, cache->num_kv_heads, D, max_context_len);
+    const int32_t chunks = pre ? prefix_chunks(pre->max_prefix_tokens) : 0;
+    const size_t need = pre ? align256(sk_bytes) + prefix_extra_bytes(num_seqs, num_q_heads, D, chunks) : sk_bytes;
     if (!workspace || workspace_bytes < need)
       return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", need, workspace ? workspace_bytes : 0);
     if (!aligned16(workspace)) return fail(PKV_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-    sk::SkParams sp;
+    sk::SkParams sp{};  // value-initialised: no suffix offsets, results to out
     sp.out = out;
     sp.q = q;
     sp.k_cache = const_cast<void*>(k_cache);  // written only when appending (pools are then the caller's writable ones)
@@ -666,8 +697,54 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
     sp.ws_acc = static_cast<float*>(workspace);
     sp.ws_ml = sp.ws_acc + recs * 16 * D;
     sp.ws_desc = reinterpret_cast<int32_t*>(sp.ws_ml + recs * 32);
-    const hipError_t err = sk::sk_launch(sp, cache->dtype, static_cast<hipStream_t>(stream));
-    if (err != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!pre) {
+      const hipError_t err = sk::sk_launch(sp, cache->dtype, st);
+      if (err != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
+      return PKV_OK;
+    }
+    // prefix-shared: prefix kernel, even split over the suffixes into fp32 partial results,
+    // then the combine writes out
+    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads;
+    unsigned char* w = static_cast<unsigned char*>(workspace) + align256(sk_bytes);
+    float* part_out = reinterpret_cast<float*>(w);
+    w += align256(rows * D * 4);
+    float* part_lse = reinterpret_cast<float*>(w);
+    w += align256(rows * 4);
+    float* pre_acc = reinterpret_cast<float*>(w);
+    w += align256(rows * chunks * D * 4);
+    float* pre_ml = reinterpret_cast<float*>(w);
+    sp.seq_start = pre->seq_prefix;
+    sp.part_out = part_out;
+    sp.part_lse = part_lse;
+    sk::PrefixParams pp{};
+    pp.q = q;
+    pp.k_cache = k_cache;
+    pp.v_cache = v_cache;
+    pp.block_tables = block_tables;
+    pp.seq_prefix = pre->seq_prefix;
+    pp.group_offsets = pre->group_offsets;
+    pp.group_members = pre->group_members;
+    pp.pre_acc = pre_acc;
+    pp.pre_ml = pre_ml;
+    pp.part_out = part_out;
+    pp.part_lse = part_lse;
+    pp.out = out;
+    pp.num_seqs = num_seqs;
+    pp.num_q_heads = num_q_heads;
+    pp.num_kv_heads = cache->num_kv_heads;
+    pp.group = G;
+    pp.head_dim = D;
+    pp.max_blocks_per_seq = max_blocks_per_seq;
+    pp.num_blocks = cache->num_blocks;
+    pp.block_size = BS;
+    pp.num_groups = pre->num_groups;
+    pp.chunks = chunks;
+    pp.scale_log2e = sp.scale_log2e;
+    hipError_t err = pre->num_groups > 0 && chunks > 0 ? sk::prefix_launch(pp, cache->dtype, st) : hipSuccess;
+    if (err == hipSuccess) err = sk::sk_launch(sp, cache->dtype, st);
+    if (err == hipSuccess) err = sk::combine_launch(pp, cache->dtype, st);
+    if (err != hipSuccess) return fail(PKV_ERR_HIP, "prefix decode launch: %s", hipGetErrorString(err));
     return PKV_OK;
   }
   const int32_t P = parts_for(max_context_len, part);
@@ -744,4 +821,29 @@ extern "C" pkv_status pkv_paged_attn_decode_append(void* out, const void* q, con
   return decode_impl(out, q, k_cache, v_cache, cache, block_tables, max_blocks_per_seq, context_lens,
                      max_context_len, num_seqs, num_q_heads, scale, workspace, workspace_bytes,
                      partition_size, stream, new_key, new_value);
+}
+
+extern "C" size_t pkv_paged_attn_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                               int32_t num_kv_heads, int32_t head_dim,
+                                                               int32_t max_context_len, int32_t max_prefix_tokens,
+                                                               int32_t dtype) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  if (max_prefix_tokens < 0 || max_prefix_tokens % 16 != 0 || max_prefix_tokens > max_context_len) return 0;
+  if (!use_stream_k(num_seqs, num_q_heads, num_kv_heads, 0, dtype)) return 0;
+  return align256(sk::sk_workspace_bytes(num_seqs, num_kv_heads, head_dim, max_context_len)) +
+         prefix_extra_bytes(num_seqs, num_q_heads, head_dim, prefix_chunks(max_prefix_tokens));
+}
+
+extern "C" pkv_status pkv_paged_attn_decode_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                                   const pkv_cache_desc* cache, const int32_t* block_tables,
+                                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                                   int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                                                   float scale, const int32_t* seq_prefix,
+                                                   const int32_t* group_offsets, const int32_t* group_members,
+                                                   int32_t num_groups, int32_t max_prefix_tokens, void* workspace,
+                                                   size_t workspace_bytes, void* stream) {
+  const PrefixArgs pre{seq_prefix, group_offsets, group_members, num_groups, max_prefix_tokens};
+  return decode_impl(out, q, k_cache, v_cache, cache, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, num_seqs, num_q_heads, scale, workspace, workspace_bytes, 0, stream, nullptr,
+                     nullptr, &pre);
 }

@@ -155,12 +155,23 @@ __device__ __forceinline__ void store_rows(typename T::raw* o, const f32x4* v, f
   wave_lds_sync();
 }
 
+// Partial-result mode: writes row r16's result (columns 16c + 4grp .. +3 in v[c], times inv)
+// as fp32, and from lane grp 0 its log2-sum-exp m + log2(l).
+template <int D>
+__device__ __forceinline__ void store_partial(const SkParams& p, int64_t row, const f32x4* v, float inv, float m,
+                                              float l, int grp) {
+  float* o = p.part_out + row * D;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) __builtin_nontemporal_store(v[c] * inv, reinterpret_cast<f32x4*>(o + 16 * c + 4 * grp));
+  if (grp == 0) p.part_lse[row] = l > 0.f ? m + __log2f(l) : -INFINITY;
+}
+
 // Per-lane tile entry of tile t (t < T): {block of rows 0-15 (8-token blocks: rows 0-7),
 // sequence, block of rows 8-15 (8-token blocks only, else -1), ntok | flags}.  A tile is 16
 // tokens of one sequence: for 16-token pool blocks one block, for 32-token blocks one half of
 // a block (kHalf: the second half), for 8-token blocks two blocks.
-template <int BS>
-__device__ __forceinline__ int4 tile_entry(const SkParams& p, const int* s_cu, int t) {
+template <int BS, bool SUFFIX>
+__device__ __forceinline__ int4 tile_entry(const SkParams& p, const int* s_cu, const int* s_start, int t) {
   int a = 0, b = p.num_seqs;  // largest a with cu[a] <= t  (cu[0] = 0 <= t < cu[B] = T)
   while (b - a > 1) {
     const int m = (a + b) >> 1;
@@ -168,26 +179,25 @@ __device__ __forceinline__ int4 tile_entry(const SkParams& p, const int* s_cu, i
   }
   const int j = t - s_cu[a];
   const int ntiles = s_cu[a + 1] - s_cu[a];
-  const int L = clamp_ctx(p.context_lens[a], p.max_context_len);
+  const int start = SUFFIX ? s_start[a] : 0;  // tokens skipped (suffix mode), a multiple of 16
+  const int L = max(0, clamp_ctx(p.context_lens[a], p.max_context_len) - start);
+  const int tok0 = start + j * kTile;  // first token of the tile in the sequence
   // The table entries are read whatever the length, so that these loads are in flight
-  // together (the indexes stay below max_blocks_per_seq whenever that is positive).  The empty
-  // tile of a sequence with no context reads nothing (block id -1) and has 0 tokens.
+  // together (indexes clamped into the row, which has max_blocks_per_seq > 0 entries whenever
+  // L > 0).  The empty tile of a sequence with no context reads nothing (block id -1) and has
+  // 0 tokens.
   const int64_t row = static_cast<int64_t>(a) * p.max_blocks_per_seq;
+  const int last = p.max_blocks_per_seq - 1;
   int e0 = -1, e1 = -1;
   if (p.max_blocks_per_seq > 0) {
-    if (BS == 16) {
-      e0 = p.block_tables[row + j];
-    } else if (BS == 32) {
-      e0 = p.block_tables[row + (j >> 1)];
-    } else {
-      e0 = p.block_tables[row + 2 * j];
-      if (2 * j + 1 < p.max_blocks_per_seq) e1 = p.block_tables[row + 2 * j + 1];
-    }
+    e0 = p.block_tables[row + min(tok0 / BS, last)];
+    if (BS == 8 && tok0 / BS + 1 <= last) e1 = p.block_tables[row + tok0 / BS + 1];
   }
   const int ntok = min(kTile, L - j * kTile);
   const int phys0 = L > 0 ? e0 : -1;
   const int phys1 = (BS == 8 && ntok > 8) ? e1 : -1;
-  const int fl = ntok | (j == ntiles - 1 ? kLast : 0) | (j == 0 ? kFirst : 0) | ((BS == 32 && (j & 1)) ? kHalf : 0);
+  const int fl = ntok | (j == ntiles - 1 ? kLast : 0) | (j == 0 ? kFirst : 0) |
+                 ((BS == 32 && ((tok0 >> 4) & 1)) ? kHalf : 0);
   return make_int4(phys0, a, phys1, fl);
 }
 
@@ -195,14 +205,16 @@ __device__ __forceinline__ int4 tile_entry(const SkParams& p, const int* s_cu, i
 // that holds the 4 waves' V tiles during the tile loop and the 8 wave states after it.
 __host__ __device__ constexpr int sk_pitch(int D) { return D == 128 ? 288 : 160; }
 __host__ __device__ inline int sk_state_bytes(int D, int G) { return ((D / 16) * 4 * G * 16 + G * 8 + 15) / 16 * 16; }
-__host__ __device__ inline int sk_cu_bytes(int B) { return ((B + 1) * 4 + 15) / 16 * 16; }
+__host__ __device__ inline int sk_cu_bytes(int B) { return ((B + 1) * 4 + 15) / 16 * 16 + (B * 4 + 15) / 16 * 16; }
 __host__ __device__ inline int sk_lds_bytes(int B, int D, int G) {
   const int tiles = kWaves * kTile * sk_pitch(D);
   const int states = 2 * kWaves * sk_state_bytes(D, G);
   return sk_cu_bytes(B) + (tiles > states ? tiles : states);
 }
 
-template <typename T, int D, int BS>
+// SUFFIX: suffix and partial-result mode (seq_start and part_out set), compiled apart so that
+// the plain decode carries none of it.
+template <typename T, int D, int BS, bool SUFFIX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_sk_kernel(SkParams p) {
   using M = Mma<T>;
@@ -229,6 +241,7 @@ void decode_sk_kernel(SkParams p) {
 
   extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
   int* s_cu = reinterpret_cast<int*>(s_dyn);                  // [B + 1]
+  int* s_start = s_cu + ((B + 1 + 3) & ~3);                    // [B] tokens skipped per sequence
   unsigned char* s_work = s_dyn + sk_cu_bytes(B);              // V tiles, later wave states
   __shared__ int s_part[kWaves];
   __shared__ int s_flags[kWaves][5];
@@ -238,8 +251,10 @@ void decode_sk_kernel(SkParams p) {
   const int lo = min(B, tid * per), hi = min(B, lo + per);
   int run = 0;
   for (int s = lo; s < hi; ++s) {
-    run += max(1, (clamp_ctx(p.context_lens[s], p.max_context_len) + kTile - 1) / kTile);
+    const int st = SUFFIX ? p.seq_start[s] : 0;
+    run += max(1, (max(0, clamp_ctx(p.context_lens[s], p.max_context_len) - st) + kTile - 1) / kTile);
     s_cu[s + 1] = run;
+    if (SUFFIX) s_start[s] = st;
   }
   // exclusive offset of this thread's sequences: a scan within the wave, then over the waves
   int incl = run;
@@ -294,7 +309,7 @@ void decode_sk_kernel(SkParams p) {
   if (n > 0) {
     // tile entries: lane i of ent holds tile t0 + kb + i, ent2 the next 64
     int kb = 0;
-    int4 ent = lane < n ? tile_entry<BS>(p, s_cu, t0 + lane) : make_int4(0, 0, 0, 0);
+    int4 ent = lane < n ? tile_entry<BS, SUFFIX>(p, s_cu, s_start, t0 + lane) : make_int4(0, 0, 0, 0);
     int4 ent2;  // read once the first tile's loads are out
 
     const int64_t tok_bytes = static_cast<int64_t>(p.num_kv_heads) * ROW;  // one token row, all heads
@@ -363,7 +378,7 @@ void decode_sk_kernel(SkParams p) {
       }
     };
     issue(0);
-    ent2 = lane + 64 < n ? tile_entry<BS>(p, s_cu, t0 + 64 + lane) : make_int4(0, 0, 0, 0);
+    ent2 = lane + 64 < n ? tile_entry<BS, SUFFIX>(p, s_cu, s_start, t0 + 64 + lane) : make_int4(0, 0, 0, 0);
 
     int cur_s = -1, seg_k0 = 0;
     bool seg_first = false;  // the current segment starts at its sequence's first tile
@@ -375,7 +390,7 @@ void decode_sk_kernel(SkParams p) {
       if (k - kb == 64) {  // slide the entry window
         kb += 64;
         ent = ent2;
-        ent2 = kb + 64 + lane < n ? tile_entry<BS>(p, s_cu, t0 + kb + 64 + lane) : make_int4(0, 0, 0, 0);
+        ent2 = kb + 64 + lane < n ? tile_entry<BS, SUFFIX>(p, s_cu, s_start, t0 + kb + 64 + lane) : make_int4(0, 0, 0, 0);
       }
       const int i = k - kb;
       const int s = lane_val(ent.y, i), fl = lane_val(ent.w, i);
@@ -461,8 +476,12 @@ void decode_sk_kernel(SkParams p) {
       const float lsum = swap32_sum(swap16_sum(l_run));
       if (seg_first && (fl & kLast)) {  // the whole sequence lies in this wave's sub-range
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        store_rows<T, D>(static_cast<raw*>(p.out) + (static_cast<int64_t>(s) * p.num_q_heads + g * G) * D, acc, inv,
-                         vt, G, lane);
+        if constexpr (SUFFIX) {
+          if (r16 < G) store_partial<D>(p, static_cast<int64_t>(s) * p.num_q_heads + g * G + r16, acc, inv, m_run, lsum, grp);
+        } else {
+          store_rows<T, D>(static_cast<raw*>(p.out) + (static_cast<int64_t>(s) * p.num_q_heads + g * G) * D, acc, inv,
+                           vt, G, lane);
+        }
       } else if (seg_k0 == 0 && !seg_first) {  // began in an earlier sub-range (A)
         hasA = true;
         a_through = !(fl & kLast);
@@ -553,9 +572,14 @@ void decode_sk_kernel(SkParams p) {
           record(0);
         } else {
           const float inv = cl > 0.f ? 1.f / cl : 0.f;
-          raw* o = static_cast<raw*>(p.out) + (static_cast<int64_t>(s_flags[w][3]) * p.num_q_heads + g * G + r16) * D;
+          const int64_t orow = static_cast<int64_t>(s_flags[w][3]) * p.num_q_heads + g * G + r16;
+          if constexpr (SUFFIX) {
+            store_partial<D>(p, orow, ca, inv, cm, cl, grp);
+          } else {
+            raw* o = static_cast<raw*>(p.out) + orow * D;
 #pragma unroll
-          for (int c = 0; c < NC; ++c) store4<T>(o + 16 * c + 4 * grp, ca[c] * inv);
+            for (int c = 0; c < NC; ++c) store4<T>(o + 16 * c + 4 * grp, ca[c] * inv);
+          }
         }
         open = false;
       }
@@ -675,9 +699,17 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
         const float f0 = __builtin_amdgcn_exp2f(m - mn), f1 = __builtin_amdgcn_exp2f(o1.x - mn);
         const float L = l * f0 + o1.y * f1;
         const float inv = L > 0.f ? 1.f / L : 0.f;
-        raw* o = static_cast<raw*>(p.out) + (static_cast<int64_t>(s) * p.num_q_heads + g * G + r16) * D;
+        const int64_t orow = static_cast<int64_t>(s) * p.num_q_heads + g * G + r16;
+        if (p.part_out) {
+          f32x4 r[NC];
 #pragma unroll
-        for (int q = 0; q < NC; ++q) store4<T>(o + 16 * q + 4 * grp, (a[q] * f0 + s_a[q * 64 + lane] * f1) * inv);
+          for (int q = 0; q < NC; ++q) r[q] = a[q] * f0 + s_a[q * 64 + lane] * f1;
+          store_partial<D>(p, orow, r, inv, mn, L, grp);
+        } else {
+          raw* o = static_cast<raw*>(p.out) + orow * D;
+#pragma unroll
+          for (int q = 0; q < NC; ++q) store4<T>(o + 16 * q + 4 * grp, (a[q] * f0 + s_a[q * 64 + lane] * f1) * inv);
+        }
       }
     }
   }
@@ -710,7 +742,10 @@ template <typename T, int D, int BS>
 hipError_t launch(const SkParams& p, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(sk_lds_bytes(p.num_seqs, D, p.group));
   const int hgroups = (p.num_kv_heads + kHeads - 1) / kHeads;
-  hipLaunchKernelGGL((decode_sk_kernel<T, D, BS>), dim3(p.ranges * hgroups), dim3(kThreads), lds, stream, p);
+  if (p.seq_start)
+    hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, true>), dim3(p.ranges * hgroups), dim3(kThreads), lds, stream, p);
+  else
+    hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, false>), dim3(p.ranges * hgroups), dim3(kThreads), lds, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((merge_sk_kernel<T, D>), dim3(p.ranges * hgroups), dim3(kMergeThreads),
@@ -723,6 +758,205 @@ hipError_t launch_bs(const SkParams& p, hipStream_t stream) {
   if (p.block_size == 8) return launch<T, D, 8>(p, stream);
   if (p.block_size == 32) return launch<T, D, 32>(p, stream);
   return launch<T, D, 16>(p, stream);
+}
+
+// ---------------------------------------------------------------------------------------
+// Prefix-shared decode.  Sequences of a group share the physical blocks of their first P
+// tokens (prefix sharing by referencing the same blocks: the yunthe.com page, section
+// "PagedAttention分页注意力机制原理"; the 111cn.net page §3.2, one block shared by several
+// requests).  Attention is a sum over tokens, so it splits exactly into the shared prefix and
+// each sequence's own suffix, merged with the log-sum-exp rule.  The prefix kernel reads each
+// prefix tile once for the whole group: a work-group takes one KV head and 16 tiles of one
+// group's prefix, and its 4 waves take the group's query rows (member x query head of that KV
+// head) 16 at a time, so they read the same K/V tiles at the same time (one HBM read, the
+// other waves served by L1/L2).
+
+template <typename T, int D, int BS>
+__global__ __launch_bounds__(256) void prefix_kernel(PrefixParams pp) {
+  using M = Mma<T>;
+  using raw = typename T::raw;
+  constexpr int ROW = D * 2;
+  constexpr int KC = D / 32;
+  constexpr int NC = D / 16;
+  constexpr int PITCH = sk_pitch(D);
+  constexpr int TILE_LDS = kTile * PITCH;
+  const int Hkv = pp.num_kv_heads, G = pp.group;
+  const int g = blockIdx.x % Hkv;
+  const int c = (blockIdx.x / Hkv) % pp.chunks;
+  const int gi = blockIdx.x / (Hkv * pp.chunks);
+  const int mo = pp.group_offsets[gi], nm = pp.group_offsets[gi + 1] - mo;
+  if (nm <= 0) return;
+  const int lead = pp.group_members[mo];
+  const int ptiles = pp.seq_prefix[lead] / kTile;
+  const int k0 = c * kPrefixChunkTiles, nk = min(ptiles - k0, kPrefixChunkTiles);
+  if (nk <= 0) return;  // uniform over the work-group
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[4 * TILE_LDS];
+  unsigned char* vt = s_v + wave * TILE_LDS;
+
+  const int64_t tok_bytes = static_cast<int64_t>(Hkv) * ROW;
+  const int64_t block_bytes = BS * tok_bytes;
+  const int voff = r16 * static_cast<int>(tok_bytes) + g * ROW + grp * 16;
+  const unsigned char* kbase = static_cast<const unsigned char*>(pp.k_cache);
+  const unsigned char* vbase = static_cast<const unsigned char*>(pp.v_cache);
+  // lane i < nk: block ids of prefix tile k0 + i (from the first member's table)
+  const int64_t trow = static_cast<int64_t>(lead) * pp.max_blocks_per_seq;
+  int e0 = -1, e1 = -1, half = 0;
+  if (lane < nk) {
+    const int tok0 = (k0 + lane) * kTile;
+    e0 = pp.block_tables[trow + tok0 / BS];
+    if (BS == 8) e1 = pp.block_tables[trow + tok0 / BS + 1];
+    if (BS == 32) half = (tok0 >> 4) & 1;
+  }
+  const int rows = nm * G;
+  const int tr_base = (4 * grp + (r16 >> 2)) * PITCH + 8 * (r16 & 3);
+  for (int rt = wave; rt * 16 < rows; rt += 4) {
+    // row r16 of this row tile: member r / G, query head g * G + r % G
+    const int r = rt * 16 + r16;
+    const bool valid = r < rows;
+    const int seq = pp.group_members[mo + (valid ? r / G : 0)];
+    const int qh = g * G + (valid ? r % G : 0);
+    const u32x4* qv = reinterpret_cast<const u32x4*>(static_cast<const raw*>(pp.q) +
+                                                     (static_cast<int64_t>(seq) * pp.num_q_heads + qh) * D);
+    typename M::v8 qb[KC];
+#pragma unroll
+    for (int cc = 0; cc < KC; ++cc) qb[cc] = __builtin_bit_cast(typename M::v8, valid ? qv[grp + 4 * cc] : u32x4{0u, 0u, 0u, 0u});
+    u32x4 kbuf[KC], vbuf[KC];
+    auto issue = [&](int kk) {
+      int phys = 0, nrec = 0, phys1 = 0, nrec1 = 0, hf = 0;
+      if (kk < nk) {
+        phys = lane_val(e0, kk);
+        nrec = (phys >= 0 && phys < pp.num_blocks) ? static_cast<int>((BS == 8 ? 8 : kTile) * tok_bytes) : 0;
+        phys = nrec ? phys : 0;
+        if (BS == 32) hf = lane_val(half, kk);
+        if (BS == 8) {
+          phys1 = lane_val(e1, kk);
+          nrec1 = (phys1 >= 0 && phys1 < pp.num_blocks) ? static_cast<int>(kTile * tok_bytes) : 0;
+          phys1 = nrec1 ? phys1 : 0;
+        }
+      }
+      const int64_t off = phys * block_bytes + hf * kTile * tok_bytes;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kbase) + off, 0, nrec, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(vbase) + off, 0, nrec, kRsrcWord3);
+      if (BS != 8 || r16 < 8) {
+#pragma unroll
+        for (int cc = 0; cc < KC; ++cc) kbuf[cc] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff + cc * 64, 0, 0);
+#pragma unroll
+        for (int cc = 0; cc < KC; ++cc) vbuf[cc] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + cc * 64, 0, 0);
+      } else {
+        const int64_t off1 = phys1 * block_bytes - 8 * tok_bytes;
+        const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kbase) + off1, 0, nrec1, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rv1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(vbase) + off1, 0, nrec1, kRsrcWord3);
+#pragma unroll
+        for (int cc = 0; cc < KC; ++cc) kbuf[cc] = __builtin_amdgcn_raw_buffer_load_b128(rk1, voff + cc * 64, 0, 0);
+#pragma unroll
+        for (int cc = 0; cc < KC; ++cc) vbuf[cc] = __builtin_amdgcn_raw_buffer_load_b128(rv1, voff + cc * 64, 0, 0);
+      }
+    };
+    float m_run = kNegBig, l_run = 0.f;
+    f32x4 acc[NC];
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) acc[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    issue(0);
+    for (int k = 0; k < nk; ++k) {
+      // every prefix tile is full (16 tokens): no masking
+#pragma unroll
+      for (int cc = 0; cc < KC; ++cc) *reinterpret_cast<u32x4*>(vt + r16 * PITCH + (grp + 4 * cc) * 16) = vbuf[cc];
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < KC; ++cc) sacc = M::qk(__builtin_bit_cast(typename M::v8, kbuf[cc]), qb[cc], sacc);
+      issue(k + 1);
+      float sv[4], mx = kNegBig;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sv[e] = sacc[e] * pp.scale_log2e;
+        mx = fmaxf(mx, sv[e]);
+      }
+      mx = swap32_max(swap16_max(mx));
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
+        const float mn = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+        l_run *= alpha;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) acc[cc] *= alpha;
+        m_run = mn;
+      }
+      i16x4_t pbits;
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const short pe = M::pack(__builtin_amdgcn_exp2f(sv[e] - m_run));
+        pbits[e] = pe;
+        psum += M::unpack(pe);
+      }
+      l_run += psum;
+      wave_lds_sync();
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + tr_base + 32 * cc));
+        acc[cc] = M::pv(vb, pbits, acc[cc]);
+      }
+      wave_lds_sync();
+    }
+    const float lsum = swap32_sum(swap16_sum(l_run));
+    if (valid) {
+      const int64_t rec = (static_cast<int64_t>(seq) * pp.num_q_heads + qh) * pp.chunks + c;
+      float* pa = pp.pre_acc + rec * D;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) __builtin_nontemporal_store(acc[cc], reinterpret_cast<f32x4*>(pa + 16 * cc + 4 * grp));
+      if (grp == 0) {
+        __builtin_nontemporal_store(m_run, pp.pre_ml + rec * 2);
+        __builtin_nontemporal_store(lsum, pp.pre_ml + rec * 2 + 1);
+      }
+    }
+  }
+}
+
+// Final result of every sequence: its suffix result (normalised, with log2-sum-exp lse) merged
+// with its group's prefix chunk partials (m_c, l_c, acc_c) in chunk order:
+//   M = max(lse, m_c),  out = (o * 2^(lse-M) + sum_c acc_c 2^(m_c-M)) / (2^(lse-M) + sum_c l_c 2^(m_c-M)).
+// One work-group per (sequence, KV head); each thread takes 4 consecutive columns of one row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void combine_kernel(PrefixParams pp) {
+  using raw = typename T::raw;
+  const int s = blockIdx.x / pp.num_kv_heads, g = blockIdx.x % pp.num_kv_heads;
+  const int G = pp.group;
+  const int nch = (pp.seq_prefix[s] / kTile + kPrefixChunkTiles - 1) / kPrefixChunkTiles;
+  for (int idx = threadIdx.x; idx < G * (D / 4); idx += 256) {
+    const int h = g * G + idx / (D / 4), col = 4 * (idx % (D / 4));
+    const int64_t row = static_cast<int64_t>(s) * pp.num_q_heads + h;
+    f32x4 o = *reinterpret_cast<const f32x4*>(pp.part_out + row * D + col);
+    const float lse = pp.part_lse[row];
+    if (nch > 0) {
+      float Mx = lse;
+      for (int c = 0; c < nch; ++c) Mx = fmaxf(Mx, pp.pre_ml[(row * pp.chunks + c) * 2]);
+      const float ws = lse == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lse - Mx);
+      f32x4 num = o * ws;
+      float den = ws;
+      for (int c = 0; c < nch; ++c) {
+        const int64_t rec = row * pp.chunks + c;
+        const float f = __builtin_amdgcn_exp2f(pp.pre_ml[rec * 2] - Mx);
+        den = fmaf(pp.pre_ml[rec * 2 + 1], f, den);
+        num += *reinterpret_cast<const f32x4*>(pp.pre_acc + rec * D + col) * f;
+      }
+      o = num * (den > 0.f ? 1.f / den : 0.f);
+    }
+    store4<T>(static_cast<raw*>(pp.out) + row * D + col, o);
+  }
+}
+
+template <typename T, int D>
+hipError_t prefix_launch_t(const PrefixParams& pp, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>(pp.num_groups) * pp.chunks * pp.num_kv_heads;
+  if (grid == 0) return hipSuccess;
+  if (pp.block_size == 8)
+    hipLaunchKernelGGL((prefix_kernel<T, D, 8>), dim3(grid), dim3(256), 0, stream, pp);
+  else if (pp.block_size == 32)
+    hipLaunchKernelGGL((prefix_kernel<T, D, 32>), dim3(grid), dim3(256), 0, stream, pp);
+  else
+    hipLaunchKernelGGL((prefix_kernel<T, D, 16>), dim3(grid), dim3(256), 0, stream, pp);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -757,6 +991,31 @@ hipError_t sk_launch(SkParams p, int32_t dtype, hipStream_t stream) {
   const int D = p.head_dim;
   if (dtype == PKV_BF16) return D == 64 ? launch_bs<BF16, 64>(p, stream) : launch_bs<BF16, 128>(p, stream);
   return D == 64 ? launch_bs<F16, 64>(p, stream) : launch_bs<F16, 128>(p, stream);
+}
+
+}  // namespace sk
+}  // namespace pkv
+
+namespace pkv {
+namespace sk {
+
+hipError_t prefix_launch(const PrefixParams& pp, int32_t dtype, hipStream_t stream) {
+  const int D = pp.head_dim;
+  if (dtype == PKV_BF16) return D == 64 ? prefix_launch_t<BF16, 64>(pp, stream) : prefix_launch_t<BF16, 128>(pp, stream);
+  return D == 64 ? prefix_launch_t<F16, 64>(pp, stream) : prefix_launch_t<F16, 128>(pp, stream);
+}
+
+hipError_t combine_launch(const PrefixParams& pp, int32_t dtype, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(pp.num_seqs) * pp.num_kv_heads);
+  const int D = pp.head_dim;
+  if (dtype == PKV_BF16) {
+    if (D == 64) hipLaunchKernelGGL((combine_kernel<BF16, 64>), grid, dim3(256), 0, stream, pp);
+    else hipLaunchKernelGGL((combine_kernel<BF16, 128>), grid, dim3(256), 0, stream, pp);
+  } else {
+    if (D == 64) hipLaunchKernelGGL((combine_kernel<F16, 64>), grid, dim3(256), 0, stream, pp);
+    else hipLaunchKernelGGL((combine_kernel<F16, 128>), grid, dim3(256), 0, stream, pp);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace sk

@@ -190,6 +190,44 @@ def test_move_seqs_matches_oracle_on_random_histories(ops, nb, nh, bs, seed):
         _same_state(pools[1], bms[1])
 
 
+def test_prefix_groups_replay_hand_worked_fixture():
+    with open(os.path.join(ROOT, "tests", "golden", "prefix_groups_worked.json"), encoding="utf-8") as f:
+        fx = json.load(f)
+    pool = B.BlockPool(fx["num_blocks"], fx["block_size"])
+    bm = BlockManager(fx["num_blocks"], fx["block_size"])
+    for op in fx["ops"]:
+        tup = {"allocate": ("allocate", op.get("seq"), 0, op.get("tokens", 0)),
+               "fork": ("fork", op.get("parent"), op.get("child"), 0),
+               "free": ("free", op.get("seq"), 0, 0),
+               "extend": ("extend", op.get("seq"), 0, op.get("n", 0))}[op["op"]]
+        _both_run(pool, bm, tup)
+    sp, offs, mem, mx = pool.prefix_groups(fx["batch"])
+    assert sp.tolist() == fx["expected_seq_prefix"]
+    assert [mem[offs[i]:offs[i + 1]].tolist() for i in range(len(offs) - 1)] == fx["expected_groups"]
+    assert mx == max(fx["expected_seq_prefix"])
+    sp, offs, mem, mx = pool.prefix_groups(fx["batch"], 48)
+    assert sp.tolist() == [0] * len(fx["batch"]) and offs.tolist() == [0] and mx == 0
+
+
+@settings(max_examples=200, deadline=None)
+@given(ops=_ops, nb=st.integers(1, 40), bs=st.sampled_from([1, 4, 8, 16, 32]), seed=st.integers(0, 1000),
+       min_prefix=st.sampled_from([0, 16, 48]))
+def test_prefix_groups_match_oracle_on_random_histories(ops, nb, bs, seed, min_prefix):
+    order = np.random.default_rng(seed).permutation(nb).astype(np.int32)
+    pool = B.BlockPool(nb, bs, order)
+    bm = BlockManager(nb, bs, order.tolist())
+    for op in ops:
+        _both_run(pool, bm, op)
+    batch = sorted(bm.block_tables)
+    if len(batch) > 1:
+        batch = batch + batch[:1]  # the same sequence twice in a batch shares everything
+    sp, offs, mem, mx = pool.prefix_groups(batch, min_prefix)
+    esp, egroups = bm.prefix_groups(batch, min_prefix)
+    assert sp.tolist() == esp
+    assert [mem[offs[i]:offs[i + 1]].tolist() for i in range(len(offs) - 1)] == egroups
+    assert mx == max(esp, default=0)
+
+
 def test_move_seqs_rejects_bad_arguments():
     a, b = B.BlockPool(4, 16), B.BlockPool(4, 8)
     lib = B.lib()

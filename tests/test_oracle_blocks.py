@@ -201,3 +201,68 @@ def test_swap_out_and_in_keeps_every_sequence_readable(seed):
                 refs[b] += 1
         assert refs == pool.ref_count
         assert sorted(pool.free_blocks + [b for b in range(pool.num_blocks) if refs[b]]) == list(range(pool.num_blocks))
+
+
+# ------------------------------------------------------------------ prefix groups
+def _replay(fx):
+    bm = BlockManager(fx["num_blocks"], fx["block_size"])
+    for op in fx["ops"]:
+        if op["op"] == "allocate":
+            bm.allocate(op["seq"], op["tokens"])
+        elif op["op"] == "fork":
+            bm.fork(op["parent"], op["child"])
+        elif op["op"] == "free":
+            bm.free(op["seq"])
+        else:
+            bm.extend(op["seq"], op["n"])
+    return bm
+
+
+def test_prefix_groups_match_hand_worked_fixture():
+    with open(os.path.join(GOLDEN, "prefix_groups_worked.json"), encoding="utf-8") as f:
+        fx = json.load(f)
+    bm = _replay(fx)
+    sp, groups = bm.prefix_groups(fx["batch"])
+    assert sp == fx["expected_seq_prefix"] and groups == fx["expected_groups"]
+    alt = fx["with_min_prefix_tokens_48"]
+    sp, groups = bm.prefix_groups(fx["batch"], 48)
+    assert sp == alt["expected_seq_prefix"] and groups == alt["expected_groups"]
+
+
+@settings(max_examples=80, deadline=None)
+@given(st.integers(min_value=0, max_value=2**31 - 1), st.sampled_from([8, 16, 32]))
+def test_prefix_groups_are_shared_and_maximal(seed, bs):
+    """Forked families with random suffixes: every group's members name the same blocks for the
+    first P tokens, P is a multiple of 16 covered by full blocks of every member, and a group's
+    common run of full shared blocks is not longer than P rounds down from."""
+    rng = np.random.default_rng(seed)
+    bm = BlockManager(400, bs, rng.permutation(400).tolist())
+    batch, sid = [], 0
+    for fam in range(int(rng.integers(1, 5))):
+        root = 10_000 + fam
+        bm.allocate(root, int(rng.integers(0, 120)))
+        for _ in range(int(rng.integers(1, 5))):
+            bm.fork(root, sid)
+            bm.extend(sid, int(rng.integers(0, 40)))
+            batch.append(sid)
+            sid += 1
+        bm.free(root)
+    order = rng.permutation(len(batch)).tolist()
+    batch = [batch[i] for i in order]
+    sp, groups = bm.prefix_groups(batch)
+    grouped = {i for g in groups for i in g}
+    for i in range(len(batch)):
+        if i not in grouped:
+            assert sp[i] == 0
+    for g in groups:
+        P = sp[g[0]]
+        assert P % 16 == 0 and P >= 16 and all(sp[i] == P for i in g) and g == sorted(g)
+        nb = P // bs if P % bs == 0 else P // bs + 1
+        tabs = [bm.block_table(batch[i]) for i in g]
+        assert all(t[:nb] == tabs[0][:nb] for t in tabs)
+        assert all(bm.context_len(batch[i]) >= P for i in g)
+        full = min(bm.context_len(batch[i]) // bs for i in g)
+        k = 0
+        while k < full and all(t[k] == tabs[0][k] for t in tabs):
+            k += 1
+        assert P == k * bs // 16 * 16
