@@ -44,21 +44,22 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(uint4* __restrict
     uint4* vd = dv + dst * block_vecs;
     for (int64_t v0 = static_cast<int64_t>(blockIdx.x) * kStepVecs; v0 < block_vecs;
          v0 += static_cast<int64_t>(gridDim.x) * kStepVecs) {
-      uint4 a[kUnroll], b[kUnroll];
+      if (v0 + kStepVecs <= block_vecs) {  // whole step: all loads in flight, then all stores
+        uint4 a[kUnroll], b[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int64_t v = v0 + u * kThreads + threadIdx.x;
-        if (v < block_vecs) {
-          a[u] = ks[v];
-          b[u] = vs[v];
+        for (int u = 0; u < kUnroll; ++u) {
+          a[u] = ks[v0 + u * kThreads + threadIdx.x];
+          b[u] = vs[v0 + u * kThreads + threadIdx.x];
         }
-      }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int64_t v = v0 + u * kThreads + threadIdx.x;
-        if (v < block_vecs) {
-          kd[v] = a[u];
-          vd[v] = b[u];
+        for (int u = 0; u < kUnroll; ++u) {
+          kd[v0 + u * kThreads + threadIdx.x] = a[u];
+          vd[v0 + u * kThreads + threadIdx.x] = b[u];
+        }
+      } else {  // tail of a block whose size is not a multiple of a step
+        for (int64_t v = v0 + threadIdx.x; v < block_vecs; v += kThreads) {
+          kd[v] = ks[v];
+          vd[v] = vs[v];
         }
       }
     }
