@@ -48,6 +48,22 @@ def algorithmic_bytes(w):
     return kv, kv + qo + tables
 
 
+def prefix_shared_bytes(w, seq_prefix, group_offsets, group_members):
+    """Bytes the prefix-shared decode must move: each group's shared prefix K/V read once per
+    group, every sequence's own remainder (with its appended token) once, q read, out written,
+    block-table entries and context lengths read.  Partial results of the prefix / suffix split
+    are not counted, as for the plain decode.  Returns (kv_bytes_read, decode_bytes)."""
+    sp = w.spec
+    e = {"float32": 4, "float16": 2, "bfloat16": 2}[sp.dtype]
+    lens = [int(L) + 1 for L in w.context_lens]
+    tokens = sum(lens) - sum(int(p) for p in seq_prefix)
+    tokens += sum(int(seq_prefix[group_members[group_offsets[g]]]) for g in range(len(group_offsets) - 1))
+    kv = tokens * sp.num_kv_heads * sp.head_dim * 2 * e
+    qo = 2 * sp.num_seqs * sp.num_q_heads * sp.head_dim * e
+    tables = 4 * sum(-(-L // 16) for L in lens) + 4 * sp.num_seqs
+    return kv, kv + qo + tables
+
+
 COUNTERS = os.path.join(ROOT, "profiles", "decode_gqa_bf16_B256_counters.md")
 SK_SOURCE = os.path.join(ROOT, "paged_kv_cache_376_amd", "csrc", "paged_attn_sk.hip")
 
@@ -399,6 +415,10 @@ def main():
             f"(p10 {np.percentile(t_dec, 10) * 1e3:.1f}, p90 {np.percentile(t_dec, 90) * 1e3:.1f})")
 
     kv_bytes, dec_bytes = algorithmic_bytes(w)
+    kv_read = kv_bytes
+    if args.prefix_shared:
+        # the method reads each shared prefix once per group: that is the roofline's byte count
+        kv_read, dec_bytes = prefix_shared_bytes(w, sp_, offs_, mem_)
     e_bytes = {"float32": 4, "float16": 2, "bfloat16": 2}[sp.dtype]
     app_bytes = 4 * sp.num_seqs * sp.num_kv_heads * sp.head_dim * e_bytes  # new rows read + written
     if not two_calls:
@@ -429,7 +449,9 @@ def main():
         "vs_baseline": None,
         "dtype": {"float32": "f32", "float16": "f16", "bfloat16": "bf16"}[sp.dtype],
         "data": "synthetic (seeded N(0,1) K/V/q, shuffled physical blocks)",
-        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        # K/V bytes actually read per step over the step time (differs from `value` only when
+        # prefixes are shared: `value` then counts every sequence's whole context)
+        "pct_hbm_peak": round(100.0 * kv_read / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s_per_layer": round(sp.num_seqs / (ms_step / 1e3), 1),
         "decode_tokens_per_s_70b_shape_attention_only": round(sp.num_seqs / (LAYERS_70B * ms_step / 1e3), 1),
         "append_us": None if t_app is None else round(float(t_app.mean()) * 1e3, 2),
@@ -444,6 +466,7 @@ def main():
             "num_seqs": sp.num_seqs,
             "kv_tokens": int(w.context_lens.sum()) + sp.num_seqs,
             "kv_bytes_per_step": kv_bytes,
+            "kv_bytes_read_per_step": kv_read,
             "partition_tokens": part if part else "even split over the GPU",
             "pool_blocks": w.num_blocks,
         },

@@ -261,7 +261,7 @@ PKV_API pkv_status pkv_paged_attn_decode_prefix(void* out, const void* q,
 
 /* Bytes of workspace pkv_paged_attn_decode_prefix needs (the even split's, plus fp32
  * suffix results [num_seqs][num_q_heads][head_dim + 1] and prefix partials
- * [num_seqs][num_q_heads][ceil(max_prefix_tokens / 256)][head_dim + 2], each region rounded up
+ * [num_seqs][num_q_heads][ceil(max_prefix_tokens / 512)][head_dim + 2], each region rounded up
  * to 256 bytes).  0 for arguments the call would reject. */
 PKV_API size_t pkv_paged_attn_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                                     int32_t num_kv_heads, int32_t head_dim,

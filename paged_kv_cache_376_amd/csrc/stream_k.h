@@ -52,7 +52,7 @@ struct SkParams {
 // (the same physical blocks) are attended once per group by the prefix kernel, the rest of
 // each context by the even split in suffix and partial-result mode, and a combine kernel merges
 // the two.
-constexpr int kPrefixChunkTiles = 16;  // 16-token tiles per prefix work-group (256 tokens)
+constexpr int kPrefixChunkTiles = 32;  // 16-token tiles per prefix work-group (512 tokens)
 
 struct PrefixParams {
   const void* q;
