@@ -65,7 +65,18 @@ def prefix_shared_bytes(w, seq_prefix, group_offsets, group_members):
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "decode_gqa_bf16_B256_counters.md")
-SK_SOURCE = os.path.join(ROOT, "paged_kv_cache_376_amd", "csrc", "paged_attn_sk.hip")
+# sources of the decode and merge kernels the counters were taken on
+SK_SOURCES = [os.path.join(ROOT, "paged_kv_cache_376_amd", "csrc", f)
+              for f in ("paged_attn_sk.hip", "tile_common.h", "stream_k.h", "dtypes.h")]
+
+
+def sk_source_sha256():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in SK_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def counter_traffic():
@@ -78,7 +89,7 @@ def counter_traffic():
         text = open(COUNTERS, encoding="utf-8").read()
         want = re.search(r"kernel_source_sha256: ([0-9a-f]{64})", text).group(1)
         value = int(re.search(r"traffic_bytes_per_call: (\d+)", text).group(1))
-        have = hashlib.sha256(open(SK_SOURCE, "rb").read()).hexdigest()
+        have = sk_source_sha256()
     except (OSError, AttributeError):
         return None
     return value if have == want else None

@@ -20,7 +20,7 @@ LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 HOST_SOURCES = ["status.cpp", "block_pool.cpp"]
-DEVICE_SOURCES = ["kv_append.hip", "paged_attn.hip", "paged_attn_sk.hip", "block_copy.hip"]
+DEVICE_SOURCES = ["kv_append.hip", "paged_attn.hip", "paged_attn_sk.hip", "block_copy.hip", "paged_attn_prefix.hip"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function"]

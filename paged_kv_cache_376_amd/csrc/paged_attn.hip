@@ -42,6 +42,7 @@
 #include "device_launch.h"
 #include "dtypes.h"
 #include "pkv_internal.h"
+#include "prefix.h"
 #include "stream_k.h"
 
 namespace pkv {

@@ -40,91 +40,26 @@
 #include "dtypes.h"
 #include "pkv_internal.h"
 #include "stream_k.h"
+#include "tile_common.h"
 
 namespace pkv {
 namespace sk {
 namespace {
 
-constexpr int kTile = 16;                 // tokens per tile (one MFMA row block)
 // Work-group shape: kHeads KV heads side by side (their waves read neighbouring slices of the
 // same token rows together) x kSplits consecutive sub-ranges of the tile list (merged in LDS).
 constexpr int kHeads = 4;
 constexpr int kSplits = 2;
 constexpr int kWaves = kHeads * kSplits;
 constexpr int kThreads = 64 * kWaves;
-constexpr float kNegBig = -1.0e30f;
-constexpr float kTau = 8.0f;              // lazy-rescale threshold (log2 units)
 constexpr int kLast = 1 << 8;             // tile flag: last tile of its sequence
 constexpr int kFirst = 1 << 9;            // tile flag: first tile of its sequence
 constexpr int kHalf = 1 << 10;            // tile flag (32-token blocks): second half of its block
-constexpr uint32_t kRsrcWord3 = 0x00020000u;  // buffer descriptor dword 3 for gfx9-class parts
-
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-
-template <typename T> struct Mma;
-template <> struct Mma<BF16> {
-  using v8 = bf16x8;
-  __device__ static f32x4 qk(v8 a, v8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
-  __device__ static f32x4 pv(i16x4_t a, i16x4_t b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-  }
-  __device__ static short pack(float x) { return __builtin_bit_cast(short, static_cast<__bf16>(x)); }
-  __device__ static float unpack(short x) { return __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(x)) << 16); }
-};
-template <> struct Mma<F16> {
-  using v8 = f16x8;
-  __device__ static f32x4 qk(v8 a, v8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
-  __device__ static f32x4 pv(i16x4_t a, i16x4_t b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
-  }
-  __device__ static short pack(float x) { return __builtin_bit_cast(short, static_cast<_Float16>(x)); }
-  __device__ static float unpack(short x) { return static_cast<float>(__builtin_bit_cast(_Float16, x)); }
-};
-
-__device__ __forceinline__ float swap16_max(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float swap32_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float swap16_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float swap32_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-// Orders one wave's LDS writes before its own later LDS reads (and vice versa).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-__device__ __forceinline__ int lane_val(int v, int i) { return __builtin_amdgcn_readlane(v, i); }
-
 __device__ __forceinline__ int clamp_ctx(int L, int maxc) { return L < 0 ? 0 : (L > maxc ? maxc : L); }
 
 // Range (within one KV head) whose tiles include tile t: the largest r with r*n/R <= t.
 __device__ __forceinline__ int range_of(int t, int n, int R) {
   return static_cast<int>(((static_cast<int64_t>(t) + 1) * R - 1) / n);
-}
-
-// Stores 4 fp32 values rounded to the element type as one 8-byte write.  Results and records
-// are written with the non-temporal hint (they are not read again by this launch's waves), which
-// keeps them from displacing K/V lines in L2.
-template <typename T>
-__device__ __forceinline__ void store4(typename T::raw* dst, f32x4 v) {
-  uint2 w;
-  w.x = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_raw(T{}, v[0]))) |
-        (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_raw(T{}, v[1]))) << 16);
-  w.y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_raw(T{}, v[2]))) |
-        (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_raw(T{}, v[3]))) << 16);
-  __builtin_nontemporal_store(static_cast<unsigned long long>(w.x) | (static_cast<unsigned long long>(w.y) << 32),
-                              reinterpret_cast<unsigned long long*>(dst));
 }
 
 // Writes a wave's G output rows, which are contiguous in memory (row r16 < G holds columns
@@ -203,7 +138,6 @@ __device__ __forceinline__ int4 tile_entry(const SkParams& p, const int* s_cu, c
 
 // LDS layout of the decode kernel (dynamic): the prefix sum of block counts, then one region
 // that holds the 4 waves' V tiles during the tile loop and the 8 wave states after it.
-__host__ __device__ constexpr int sk_pitch(int D) { return D == 128 ? 288 : 160; }
 __host__ __device__ inline int sk_state_bytes(int D, int G) { return ((D / 16) * 4 * G * 16 + G * 8 + 15) / 16 * 16; }
 __host__ __device__ inline int sk_cu_bytes(int B) { return ((B + 1) * 4 + 15) / 16 * 16 + (B * 4 + 15) / 16 * 16; }
 __host__ __device__ inline int sk_lds_bytes(int B, int D, int G) {
@@ -760,252 +694,6 @@ hipError_t launch_bs(const SkParams& p, hipStream_t stream) {
   return launch<T, D, 16>(p, stream);
 }
 
-// ---------------------------------------------------------------------------------------
-// Prefix-shared decode.  Sequences of a group share the physical blocks of their first P
-// tokens (prefix sharing by referencing the same blocks: the yunthe.com page, section
-// "PagedAttention分页注意力机制原理"; the 111cn.net page §3.2, one block shared by several
-// requests).  Attention is a sum over tokens, so it splits exactly into the shared prefix and
-// each sequence's own suffix, merged with the log-sum-exp rule.  The prefix kernel reads each
-// prefix tile once for the whole group: a work-group takes one KV head and up to 32 tiles of
-// one group's prefix.  In steps of 8 tiles, each of its 8 waves loads one tile (K and V) into
-// LDS, and then every wave runs its 16 query rows (member x query head of that KV head) over
-// the step's 8 tiles.  The LDS tiles are double-buffered (144 KiB at D 128, one work-group per
-// CU): the next step's loads are in flight while the current step is computed, so one barrier
-// per step orders the reuse.  A group with more than 128 rows repeats the pass for each
-// further 128 rows.  (8 waves and 32-tile chunks measured faster than 4 waves and 16-tile
-// chunks at two work-groups per CU: twice the bytes per step, half the partial records.)
-
-constexpr int kPrefixWaves = 8;  // waves per work-group = tiles per step
-
-template <typename T, int D, int BS>
-__global__ __launch_bounds__(64 * kPrefixWaves) void prefix_kernel(PrefixParams pp) {
-  constexpr int kPrefixStep = kPrefixWaves;
-  constexpr int kRowBlock = 16 * kPrefixWaves;  // query rows per pass
-  using M = Mma<T>;
-  using raw = typename T::raw;
-  constexpr int ROW = D * 2;
-  constexpr int KC = D / 32;
-  constexpr int NC = D / 16;
-  constexpr int PITCH = sk_pitch(D);
-  constexpr int TILE_LDS = kTile * PITCH;
-  const int Hkv = pp.num_kv_heads, G = pp.group;
-  const int g = blockIdx.x % Hkv;
-  const int c = (blockIdx.x / Hkv) % pp.chunks;
-  const int gi = blockIdx.x / (Hkv * pp.chunks);
-  const int mo = pp.group_offsets[gi], nm = pp.group_offsets[gi + 1] - mo;
-  if (nm <= 0) return;
-  const int lead = pp.group_members[mo];
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
-  const int k0 = c * kPrefixChunkTiles;
-  // lane i < kPrefixChunkTiles: block ids of chunk tile i (from the first member's table), read
-  // alongside the prefix length rather than after it; entries past the prefix are never used
-  const int64_t trow = static_cast<int64_t>(lead) * pp.max_blocks_per_seq;
-  int e0 = -1, e1 = -1, half = 0;
-  {
-    const int tok0 = (k0 + lane) * kTile;
-    const int bi = tok0 / BS;
-    if (lane < kPrefixChunkTiles && bi + (BS == 8 ? 1 : 0) < pp.max_blocks_per_seq) {
-      e0 = pp.block_tables[trow + bi];
-      if (BS == 8) e1 = pp.block_tables[trow + bi + 1];
-    }
-    if (BS == 32) half = (tok0 >> 4) & 1;
-  }
-  const int ptiles = pp.seq_prefix[lead] / kTile;
-  const int nk = min(ptiles - k0, kPrefixChunkTiles);
-  if (nk <= 0) return;  // uniform over the work-group
-  // [2 buffers][4 tiles][K tile, V tile], rows at PITCH
-  __shared__ __attribute__((aligned(16))) unsigned char s_t[2 * kPrefixStep * 2 * TILE_LDS];
-
-  const int64_t tok_bytes = static_cast<int64_t>(Hkv) * ROW;
-  const int64_t block_bytes = BS * tok_bytes;
-  const int voff = r16 * static_cast<int>(tok_bytes) + g * ROW + grp * 16;
-  const unsigned char* kbase = static_cast<const unsigned char*>(pp.k_cache);
-  const unsigned char* vbase = static_cast<const unsigned char*>(pp.v_cache);
-  const int nsteps = (nk + kPrefixStep - 1) / kPrefixStep;
-  const int rows = nm * G;
-  const int lds_slot = r16 * PITCH + grp * 16;  // this lane's 16 bytes of a tile row (+ 64 cc)
-  const int tr_base = (4 * grp + (r16 >> 2)) * PITCH + 8 * (r16 & 3);
-
-  u32x4 kbuf[KC], vbuf[KC];
-  // Loads chunk tile kk (wave-uniform) into kbuf / vbuf; past the chunk's end a zero-length load.
-  auto issue = [&](int kk) {
-    int phys = 0, nrec = 0, phys1 = 0, nrec1 = 0, hf = 0;
-    if (kk < nk) {
-      phys = lane_val(e0, kk);
-      nrec = (phys >= 0 && phys < pp.num_blocks) ? static_cast<int>((BS == 8 ? 8 : kTile) * tok_bytes) : 0;
-      phys = nrec ? phys : 0;
-      if (BS == 32) hf = lane_val(half, kk);
-      if (BS == 8) {
-        phys1 = lane_val(e1, kk);
-        nrec1 = (phys1 >= 0 && phys1 < pp.num_blocks) ? static_cast<int>(kTile * tok_bytes) : 0;
-        phys1 = nrec1 ? phys1 : 0;
-      }
-    }
-    const int64_t off = phys * block_bytes + hf * kTile * tok_bytes;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kbase) + off, 0, nrec, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(vbase) + off, 0, nrec, kRsrcWord3);
-    if (BS != 8 || r16 < 8) {
-#pragma unroll
-      for (int cc = 0; cc < KC; ++cc) kbuf[cc] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff + cc * 64, 0, 0);
-#pragma unroll
-      for (int cc = 0; cc < KC; ++cc) vbuf[cc] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + cc * 64, 0, 0);
-    } else {
-      // rows 8-15 of the tile are rows 0-7 of the second 8-token block
-      const int64_t off1 = phys1 * block_bytes - 8 * tok_bytes;
-      const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kbase) + off1, 0, nrec1, kRsrcWord3);
-      const __amdgpu_buffer_rsrc_t rv1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(vbase) + off1, 0, nrec1, kRsrcWord3);
-#pragma unroll
-      for (int cc = 0; cc < KC; ++cc) kbuf[cc] = __builtin_amdgcn_raw_buffer_load_b128(rk1, voff + cc * 64, 0, 0);
-#pragma unroll
-      for (int cc = 0; cc < KC; ++cc) vbuf[cc] = __builtin_amdgcn_raw_buffer_load_b128(rv1, voff + cc * 64, 0, 0);
-    }
-  };
-  // Writes this wave's loaded tile into LDS buffer b, tile slot `wave`.
-  auto stash = [&](int b) {
-    unsigned char* kt = s_t + (b * kPrefixStep + wave) * 2 * TILE_LDS;
-#pragma unroll
-    for (int cc = 0; cc < KC; ++cc) *reinterpret_cast<u32x4*>(kt + lds_slot + cc * 64) = kbuf[cc];
-#pragma unroll
-    for (int cc = 0; cc < KC; ++cc) *reinterpret_cast<u32x4*>(kt + TILE_LDS + lds_slot + cc * 64) = vbuf[cc];
-  };
-
-  for (int rb = 0; rb * kRowBlock < rows; ++rb) {
-    if (rb > 0) __syncthreads();  // the previous pass's last step is read from buffer 0 or 1
-    // row r16 of this wave's row tile: member r / G, query head g * G + r % G
-    const int rt0 = rb * kRowBlock + wave * 16;
-    const bool has_rows = rt0 < rows;  // wave-uniform
-    const int r = rt0 + r16;
-    const bool valid = r < rows;
-    const int seq = pp.group_members[mo + (valid ? r / G : 0)];
-    const int qh = g * G + (valid ? r % G : 0);
-    const u32x4* qv = reinterpret_cast<const u32x4*>(static_cast<const raw*>(pp.q) +
-                                                     (static_cast<int64_t>(seq) * pp.num_q_heads + qh) * D);
-    typename M::v8 qb[KC];
-#pragma unroll
-    for (int cc = 0; cc < KC; ++cc) qb[cc] = __builtin_bit_cast(typename M::v8, valid ? qv[grp + 4 * cc] : u32x4{0u, 0u, 0u, 0u});
-    float m_run = kNegBig, l_run = 0.f;
-    f32x4 acc[NC];
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) acc[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    issue(wave);
-    for (int j = 0; j < nsteps; ++j) {
-      stash(j & 1);
-      __syncthreads();
-      issue((j + 1) * kPrefixStep + wave);
-      if (!has_rows) continue;
-      const int nt = min(kPrefixStep, nk - j * kPrefixStep);
-      for (int t = 0; t < nt; ++t) {
-        // every prefix tile is full (16 tokens): no masking
-        const unsigned char* kt = s_t + ((j & 1) * kPrefixStep + t) * 2 * TILE_LDS;
-        const unsigned char* vt = kt + TILE_LDS;
-        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int cc = 0; cc < KC; ++cc)
-          sacc = M::qk(__builtin_bit_cast(typename M::v8, *reinterpret_cast<const u32x4*>(kt + lds_slot + cc * 64)), qb[cc], sacc);
-        float sv[4], mx = kNegBig;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sv[e] = sacc[e] * pp.scale_log2e;
-          mx = fmaxf(mx, sv[e]);
-        }
-        mx = swap32_max(swap16_max(mx));
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
-          const float mn = fmaxf(m_run, mx);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-          l_run *= alpha;
-#pragma unroll
-          for (int cc = 0; cc < NC; ++cc) acc[cc] *= alpha;
-          m_run = mn;
-        }
-        i16x4_t pbits;
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const short pe = M::pack(__builtin_amdgcn_exp2f(sv[e] - m_run));
-          pbits[e] = pe;
-          psum += M::unpack(pe);
-        }
-        l_run += psum;
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-          const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + tr_base + 32 * cc));
-          acc[cc] = M::pv(vb, pbits, acc[cc]);
-        }
-      }
-    }
-    const float lsum = swap32_sum(swap16_sum(l_run));
-    if (valid) {
-      const int64_t rec = (static_cast<int64_t>(seq) * pp.num_q_heads + qh) * pp.chunks + c;
-      float* pa = pp.pre_acc + rec * D;
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) __builtin_nontemporal_store(acc[cc], reinterpret_cast<f32x4*>(pa + 16 * cc + 4 * grp));
-      if (grp == 0) {
-        __builtin_nontemporal_store(m_run, pp.pre_ml + rec * 2);
-        __builtin_nontemporal_store(lsum, pp.pre_ml + rec * 2 + 1);
-      }
-    }
-  }
-}
-
-// Final result of every sequence: its suffix result (normalised, with log2-sum-exp lse) merged
-// with its group's prefix chunk partials (m_c, l_c, acc_c) in chunk order, as a running
-// log-sum-exp merge:  M' = max(M, m_c),  num' = num 2^(M-M') + acc_c 2^(m_c-M'),
-// den' = den 2^(M-M') + l_c 2^(m_c-M');  out = num / den.
-// One work-group per (sequence, KV head); each thread takes 4 consecutive columns of one row.
-// The chunk partials are loaded 4 at a time (indices clamped to the last chunk, so the loads
-// are unconditional and go out together).
-template <typename T, int D>
-__global__ __launch_bounds__(256) void combine_kernel(PrefixParams pp) {
-  using raw = typename T::raw;
-  const int s = blockIdx.x / pp.num_kv_heads, g = blockIdx.x % pp.num_kv_heads;
-  const int G = pp.group;
-  const int nch = (pp.seq_prefix[s] / kTile + kPrefixChunkTiles - 1) / kPrefixChunkTiles;
-  for (int idx = threadIdx.x; idx < G * (D / 4); idx += 256) {
-    const int h = g * G + idx / (D / 4), col = 4 * (idx % (D / 4));
-    const int64_t row = static_cast<int64_t>(s) * pp.num_q_heads + h;
-    f32x4 num = *reinterpret_cast<const f32x4*>(pp.part_out + row * D + col);
-    const float lse = pp.part_lse[row];
-    float Mx = lse, den = lse == -INFINITY ? 0.f : 1.f;
-    for (int c0 = 0; c0 < nch; c0 += 4) {
-      float mc[4], lc[4];
-      f32x4 ac[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t rec = row * pp.chunks + min(c0 + u, nch - 1);
-        mc[u] = pp.pre_ml[rec * 2];
-        lc[u] = pp.pre_ml[rec * 2 + 1];
-        ac[u] = *reinterpret_cast<const f32x4*>(pp.pre_acc + rec * D + col);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (c0 + u >= nch) break;
-        const float mn = fmaxf(Mx, mc[u]);
-        const float f0 = den > 0.f ? __builtin_amdgcn_exp2f(Mx - mn) : 0.f;
-        const float f1 = __builtin_amdgcn_exp2f(mc[u] - mn);
-        num = num * f0 + ac[u] * f1;
-        den = den * f0 + lc[u] * f1;
-        Mx = mn;
-      }
-    }
-    num = num * (den > 0.f ? 1.f / den : 0.f);
-    store4<T>(static_cast<raw*>(pp.out) + row * D + col, num);
-  }
-}
-
-template <typename T, int D>
-hipError_t prefix_launch_t(const PrefixParams& pp, hipStream_t stream) {
-  const unsigned grid = static_cast<unsigned>(pp.num_groups) * pp.chunks * pp.num_kv_heads;
-  if (grid == 0) return hipSuccess;
-  if (pp.block_size == 8)
-    hipLaunchKernelGGL((prefix_kernel<T, D, 8>), dim3(grid), dim3(64 * kPrefixWaves), 0, stream, pp);
-  else if (pp.block_size == 32)
-    hipLaunchKernelGGL((prefix_kernel<T, D, 32>), dim3(grid), dim3(64 * kPrefixWaves), 0, stream, pp);
-  else
-    hipLaunchKernelGGL((prefix_kernel<T, D, 16>), dim3(grid), dim3(64 * kPrefixWaves), 0, stream, pp);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
@@ -1038,31 +726,6 @@ hipError_t sk_launch(SkParams p, int32_t dtype, hipStream_t stream) {
   const int D = p.head_dim;
   if (dtype == PKV_BF16) return D == 64 ? launch_bs<BF16, 64>(p, stream) : launch_bs<BF16, 128>(p, stream);
   return D == 64 ? launch_bs<F16, 64>(p, stream) : launch_bs<F16, 128>(p, stream);
-}
-
-}  // namespace sk
-}  // namespace pkv
-
-namespace pkv {
-namespace sk {
-
-hipError_t prefix_launch(const PrefixParams& pp, int32_t dtype, hipStream_t stream) {
-  const int D = pp.head_dim;
-  if (dtype == PKV_BF16) return D == 64 ? prefix_launch_t<BF16, 64>(pp, stream) : prefix_launch_t<BF16, 128>(pp, stream);
-  return D == 64 ? prefix_launch_t<F16, 64>(pp, stream) : prefix_launch_t<F16, 128>(pp, stream);
-}
-
-hipError_t combine_launch(const PrefixParams& pp, int32_t dtype, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(pp.num_seqs) * pp.num_kv_heads);
-  const int D = pp.head_dim;
-  if (dtype == PKV_BF16) {
-    if (D == 64) hipLaunchKernelGGL((combine_kernel<BF16, 64>), grid, dim3(256), 0, stream, pp);
-    else hipLaunchKernelGGL((combine_kernel<BF16, 128>), grid, dim3(256), 0, stream, pp);
-  } else {
-    if (D == 64) hipLaunchKernelGGL((combine_kernel<F16, 64>), grid, dim3(256), 0, stream, pp);
-    else hipLaunchKernelGGL((combine_kernel<F16, 128>), grid, dim3(256), 0, stream, pp);
-  }
-  return hipGetLastError();
 }
 
 }  // namespace sk

@@ -1,0 +1,50 @@
+// Internal interface of the prefix-shared decode (paged_attn_prefix.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace pkv {
+namespace sk {
+
+// Prefix-shared decode: the tokens a group of sequences shares at the start of its contexts
+// (the same physical blocks) are attended once per group by the prefix kernel, the rest of
+// each context by the even split in suffix and partial-result mode, and a combine kernel merges
+// the two.
+constexpr int kPrefixChunkTiles = 32;  // 16-token tiles per prefix work-group (512 tokens)
+
+struct PrefixParams {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_prefix;     // [B] shared prefix tokens of each sequence (multiple of 16), 0 if none
+  const int32_t* group_offsets;  // [num_groups + 1] into group_members
+  const int32_t* group_members;  // batch positions; the first member's table holds the prefix blocks
+  float* pre_acc;                // [B][Hq][chunks][D] unnormalised prefix partials
+  float* pre_ml;                 // [B][Hq][chunks][2] (running max, sum)
+  const float* part_out;         // suffix results of the even split (normalised fp32) ...
+  const float* part_lse;         // ... and their log2-sum-exp
+  void* out;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t head_dim;
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_groups;
+  int32_t chunks;  // prefix work-groups per group and KV head: ceil(max prefix tiles / kPrefixChunkTiles)
+  float scale_log2e;
+};
+
+// Enqueues the prefix kernel (grid num_groups * chunks * Hkv).
+hipError_t prefix_launch(const PrefixParams& pp, int32_t dtype, hipStream_t stream);
+// Enqueues the combine kernel (prefix partials + suffix results -> out).
+hipError_t combine_launch(const PrefixParams& pp, int32_t dtype, hipStream_t stream);
+
+}  // namespace sk
+}  // namespace pkv
