@@ -86,3 +86,23 @@ def test_block_size_refused_where_not_implemented():
     with pytest.raises(binding.PkvError) as e:
         decode_step(w, partition_size=64)
     assert e.value.status_name == "PKV_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("name", ["gqa_bf16", "mha_fp16"])
+def test_block_size_full_size_sampled(name, bs):
+    """The benchmark's fused call at full size with 8- and 32-token blocks (bench.py
+    --block-size): every output finite, sampled sequences (longest, shortest, 6 random)
+    against the oracle."""
+    say(f"[block size {bs} full] {name}")
+    w = W.make_workload(name, 0, block_size=bs)
+    out, *_ = decode_step_fused(w)
+    assert torch.isfinite(out.float()).all()
+    lens = w.context_lens
+    rng = np.random.default_rng(37)
+    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
+    pick |= set(rng.choice(w.spec.num_seqs, size=6, replace=False).tolist())
+    seqs = sorted(pick)
+    err = max_err(out[seqs], oracle_out(w, seqs))
+    say(f"    sampled seqs {seqs}: max abs err {err:.3e}")
+    assert err <= TOL[w.spec.dtype]

@@ -200,3 +200,49 @@ def test_sequences_swap_out_and_back_decode_bitwise_equal():
     err = max_err(second, ref)
     say(f"    max abs err {err:.3e}")
     assert err <= TOL["bfloat16"]
+
+
+def _int_pool(rng, nb, shape):
+    return torch.from_numpy(rng.integers(-32768, 32767, size=(nb,) + shape, dtype=np.int16, endpoint=True))
+
+
+def test_copy_blocks_bench_size():
+    """The benchmark's copy (bench.py --op copy_blocks): 4096 pairs of 16 x 8 x 128 bf16 blocks
+    in a 16384-block pool, bit for bit against the oracle's copy over the whole pool."""
+    say("[copy_blocks] bench size: 4096 pairs, 16384 blocks of 32 KiB")
+    rng = np.random.default_rng(0)
+    nb, n, shape = 16384, 4096, (16, 8, 128)
+    k, v = _int_pool(rng, nb, shape), _int_pool(rng, nb, shape)
+    perm = rng.permutation(nb)
+    pairs = np.stack([perm[:n], perm[n:2 * n]], axis=1).astype(np.int32)
+    ek, ev = oracle.copy_blocks(k.numpy(), v.numpy(), pairs.tolist())
+    kd, vd = k.view(torch.bfloat16).to(DEVICE), v.view(torch.bfloat16).to(DEVICE)
+    binding.copy_blocks(kd, vd, torch.from_numpy(pairs).to(DEVICE))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(kd), ek) and np.array_equal(_bits(vd), ev)
+
+
+def test_swap_bench_size():
+    """The benchmark's swap (bench.py --op swap): 2048 blocks of 32 KiB from an 8192-block
+    device pool out to a 4096-block pinned host pool and back to other device ids, bit for bit
+    against the oracle's swaps."""
+    say("[swap] bench size: 2048 blocks out and back")
+    rng = np.random.default_rng(1)
+    nb, nh, n, shape = 8192, 4096, 2048, (16, 8, 128)
+    k, v = _int_pool(rng, nb, shape), _int_pool(rng, nb, shape)
+    kd, vd = k.view(torch.bfloat16).to(DEVICE), v.view(torch.bfloat16).to(DEVICE)
+    hk0, hv0 = _int_pool(rng, nh, shape), _int_pool(rng, nh, shape)
+    hk, hv = hk0.view(torch.bfloat16).pin_memory(), hv0.view(torch.bfloat16).pin_memory()
+    dev_ids = rng.permutation(nb)[:n]
+    host_ids = rng.permutation(nh)[:n]
+    out_pairs = np.stack([dev_ids, host_ids], axis=1).astype(np.int32)
+    ehk, ehv = oracle.swap_blocks(hk0.numpy(), hv0.numpy(), k.numpy(), v.numpy(), out_pairs.tolist())
+    binding.swap_blocks(hk, hv, kd, vd, torch.from_numpy(out_pairs).to(DEVICE))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(hk), ehk) and np.array_equal(_bits(hv), ehv)
+    back_ids = rng.permutation(nb)[:n]
+    in_pairs = np.stack([host_ids, back_ids], axis=1).astype(np.int32)
+    ebk, ebv = oracle.swap_blocks(k.numpy(), v.numpy(), ehk, ehv, in_pairs.tolist())
+    binding.swap_blocks(kd, vd, hk, hv, torch.from_numpy(in_pairs).to(DEVICE))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(kd), ebk) and np.array_equal(_bits(vd), ebv)

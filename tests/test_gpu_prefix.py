@@ -154,3 +154,25 @@ def test_prefix_decode_empty_suffixes():
     err2 = max_err(out2.cpu(), ref2)
     say(f"    suffixes 0 / 5 / 16 tokens: max abs err {err2:.3e}")
     assert err2 <= TOL["bfloat16"]
+
+
+def test_prefix_decode_full_size_sampled():
+    """The benchmark's prefix-shared step at full size (prefix_bf16: 16 groups of 8 sharing
+    1024 tokens, separate append, groups from the host pool): every output finite and within
+    tolerance of the plain decode, sampled sequences (longest, shortest, 6 random, and every
+    member of one group) against the oracle."""
+    say("[prefix decode] full size prefix_bf16")
+    w = W.make_workload("prefix_bf16", 0)
+    out, (sp, offs, mem, mx), plain, _ = _prefix_decode(w)
+    assert len(offs) - 1 == 16 and mx == 1024
+    assert torch.isfinite(out.float()).all()
+    assert float((out.double() - plain.double()).abs().max()) <= TOL["bfloat16"]
+    lens = w.context_lens
+    rng = np.random.default_rng(19)
+    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
+    pick |= set(rng.choice(w.spec.num_seqs, size=6, replace=False).tolist())
+    pick |= set(int(m) for m in mem[offs[5]:offs[6]])
+    seqs = sorted(pick)
+    err = max_err(out[seqs], oracle_out(w, seqs))
+    say(f"    sampled seqs {seqs}: max abs err {err:.3e}")
+    assert err <= TOL["bfloat16"]
