@@ -244,7 +244,12 @@ PKV_API pkv_status pkv_paged_attn_decode_append(void* out, const void* q,
  *   workspace      >= pkv_paged_attn_decode_prefix_workspace_bytes(...) bytes
  * Device-side contract: the members of a group have the same seq_prefix P <= their context
  * lengths, and the first P tokens of their tables name the same blocks (the kernels read a
- * group's prefix through its first member's table); sequences in no group have 0.
+ * group's prefix through its first member's table); sequences in no group have 0; each batch
+ * position is in at most one group.  As for the other arguments, a description that breaks
+ * this contract gives unspecified output but no access outside the buffers: offsets past
+ * num_seqs and member positions outside [0, num_seqs) are skipped, prefix lengths are kept
+ * inside [0, context length] on a 16-token boundary, and no more than
+ * ceil(max_prefix_tokens / 512) prefix partials are read per row.
  * Errors: as pkv_paged_attn_decode; UNSUPPORTED for f32 pools or more than 8192 sequences;
  * INVALID_ARGUMENT for a bad group description (null pointers, num_groups < 0, bad
  * max_prefix_tokens). */

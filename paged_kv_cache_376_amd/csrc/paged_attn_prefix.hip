@@ -43,8 +43,10 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void prefix_kernel(PrefixParams 
   const int c = (blockIdx.x / Hkv) % pp.chunks;
   const int gi = blockIdx.x / (Hkv * pp.chunks);
   const int mo = pp.group_offsets[gi], nm = pp.group_offsets[gi + 1] - mo;
-  if (nm <= 0) return;
+  // a batch position belongs to at most one group, so no member list reaches past num_seqs
+  if (nm <= 0 || mo < 0 || mo + nm > pp.num_seqs) return;
   const int lead = pp.group_members[mo];
+  if (lead < 0 || lead >= pp.num_seqs) return;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int k0 = c * kPrefixChunkTiles;
@@ -126,8 +128,9 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void prefix_kernel(PrefixParams 
     const int rt0 = rb * kRowBlock + wave * 16;
     const bool has_rows = rt0 < rows;  // wave-uniform
     const int r = rt0 + r16;
-    const bool valid = r < rows;
-    const int seq = pp.group_members[mo + (valid ? r / G : 0)];
+    int seq = pp.group_members[mo + (r < rows ? r / G : 0)];
+    const bool valid = r < rows && seq >= 0 && seq < pp.num_seqs;  // rows of invalid members are skipped
+    seq = valid ? seq : lead;
     const int qh = g * G + (valid ? r % G : 0);
     const u32x4* qv = reinterpret_cast<const u32x4*>(static_cast<const raw*>(pp.q) +
                                                      (static_cast<int64_t>(seq) * pp.num_q_heads + qh) * D);
@@ -210,7 +213,8 @@ __global__ __launch_bounds__(256) void combine_kernel(PrefixParams pp) {
   using raw = typename T::raw;
   const int s = blockIdx.x / pp.num_kv_heads, g = blockIdx.x % pp.num_kv_heads;
   const int G = pp.group;
-  const int nch = (pp.seq_prefix[s] / kTile + kPrefixChunkTiles - 1) / kPrefixChunkTiles;
+  // chunks of this sequence's prefix, never more than the workspace holds
+  const int nch = min(pp.chunks, (max(pp.seq_prefix[s], 0) / kTile + kPrefixChunkTiles - 1) / kPrefixChunkTiles);
   for (int idx = threadIdx.x; idx < G * (D / 4); idx += 256) {
     const int h = g * G + idx / (D / 4), col = 4 * (idx % (D / 4));
     const int64_t row = static_cast<int64_t>(s) * pp.num_q_heads + h;

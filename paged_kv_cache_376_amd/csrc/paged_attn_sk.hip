@@ -185,8 +185,11 @@ void decode_sk_kernel(SkParams p) {
   const int lo = min(B, tid * per), hi = min(B, lo + per);
   int run = 0;
   for (int s = lo; s < hi; ++s) {
-    const int st = SUFFIX ? p.seq_start[s] : 0;
-    run += max(1, (max(0, clamp_ctx(p.context_lens[s], p.max_context_len) - st) + kTile - 1) / kTile);
+    const int L = clamp_ctx(p.context_lens[s], p.max_context_len);
+    // suffix mode: the skipped tokens, kept inside [0, L] and on a tile boundary whatever the
+    // caller passed, so that every table index below stays inside the sequence's row
+    const int st = SUFFIX ? (min(max(p.seq_start[s], 0), L) & ~(kTile - 1)) : 0;
+    run += max(1, (max(0, L - st) + kTile - 1) / kTile);
     s_cu[s + 1] = run;
     if (SUFFIX) s_start[s] = st;
   }

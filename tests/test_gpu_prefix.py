@@ -176,3 +176,36 @@ def test_prefix_decode_full_size_sampled():
     err = max_err(out[seqs], oracle_out(w, seqs))
     say(f"    sampled seqs {seqs}: max abs err {err:.3e}")
     assert err <= TOL["bfloat16"]
+
+
+def test_prefix_decode_ignores_out_of_range_group_entries():
+    """The kernels' own bounds checks on the group description: a member position outside the
+    batch (its rows are skipped), a negative prefix length on a sequence in no group (read as
+    0), and a group whose offsets run past num_seqs (skipped).  Every real sequence still
+    matches the oracle."""
+    say("[prefix decode] out-of-range group entries")
+    spec = W.SPECS["prefix_bf16"].replace(num_seqs=12, group_size=4, prefix_len=96, suffix_hi=60)
+    w = W.Workload(spec, seed=48)
+    cache = build_cache(w, DEVICE, fill=float("nan"))
+    seqs = list(range(spec.num_seqs))
+    cache.append_tokens(seqs, w.new_k, w.new_v)
+    batch = list(range(8)) + [11]  # groups {0..3}, {4..7}; 11 alone (its group mates left out)
+    bt, ctx, maxc = cache.tables(batch)
+    sp, offs, mem, mx = cache.pool.prefix_groups(batch)
+    assert list(offs) == [0, 4, 8] and sp[8] == 0 and mx == 96
+    B = len(batch)
+    # group 0 gains a member position outside the batch; a third group runs past num_seqs (its
+    # member entries exist, so only the kernel's offset check keeps it out)
+    mem2 = np.concatenate([mem[:4], [B + 3], mem[4:], [0] * 8]).astype(np.int32)
+    offs2 = np.array([0, 5, 9, B + 5], dtype=np.int32)
+    sp2 = sp.copy()
+    sp2[8] = -16  # negative prefix length on the sequence in no group
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEVICE)
+    q = w.q[batch].to(DEVICE).contiguous()
+    out = torch.empty_like(q)
+    binding.paged_attn_decode_prefix(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale,
+                                     dev(sp2), dev(offs2), dev(mem2), mx)
+    torch.cuda.synchronize()
+    err = max_err(out.cpu(), oracle_out(w, batch))
+    say(f"    max abs err {err:.3e}")
+    assert err <= TOL["bfloat16"]
