@@ -151,6 +151,27 @@ def _same(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _on_device(device, *ts):
+    """Index arrays the kernels read (tables, lengths, slots, pairs) must live on the launch
+    device: a host tensor's pointer would reach the GPU as an address it cannot read."""
+    for t in ts:
+        if t.device != device:
+            raise ValueError(f"a {tuple(t.shape)} tensor is on {t.device}, not on {device}")
+
+
+def _workspace(nbytes, device, stream):
+    """A workspace from torch's caching allocator, allocated on the stream the call is launched
+    on, so that the allocator does not hand its memory out again before that stream has run
+    the call."""
+    import torch
+
+    if stream is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    s = torch.cuda.ExternalStream(stream, device=device) if isinstance(stream, int) else stream
+    with torch.cuda.stream(s):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def kv_cache_append(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
     """pkv_kv_cache_append: key/value [T, Hkv, D] into the pools at int64 slot_mapping [T]."""
     import torch
@@ -166,6 +187,7 @@ def kv_cache_append(key, value, k_cache, v_cache, slot_mapping, stream=None) -> 
         raise ValueError("key/value must be [T, Hkv, D]")
     if slot_mapping.numel() != T:
         raise ValueError("slot_mapping must have T entries")
+    _on_device(k_cache.device, slot_mapping)
     _check(lib().pkv_kv_cache_append(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
                                       ctypes.byref(desc), _ptr(slot_mapping), T, _stream(stream)))
 
@@ -184,6 +206,7 @@ def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
     if tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("k_cache and v_cache shapes differ")
     n = _pairs_arg(pairs)
+    _on_device(k_cache.device, pairs)
     desc = cache_desc(k_cache)
     _check(lib().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(pairs), n, _stream(stream)))
 
@@ -241,9 +264,10 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_
         raise ValueError("block_tables must be contiguous [B, max_blocks_per_seq]")
     if context_lens.numel() != B or not context_lens.is_contiguous():
         raise ValueError("context_lens must be contiguous [B]")
+    _on_device(q.device, block_tables, context_lens)
     need = paged_attn_workspace_bytes(B, Hq, desc.num_kv_heads, D, max_context_len, partition_size, desc.dtype)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pkv_paged_attn_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
@@ -275,11 +299,14 @@ def paged_attn_decode_prefix(out, q, k_cache, v_cache, block_tables, context_len
             raise ValueError("tables, lengths and group arrays must be contiguous int32")
     if seq_prefix.numel() != B or group_offsets.numel() < 1:
         raise ValueError("seq_prefix must have B entries, group_offsets at least one")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables must be [B, max_blocks_per_seq] and context_lens [B]")
+    _on_device(q.device, block_tables, context_lens, seq_prefix, group_offsets, group_members)
     ng = group_offsets.numel() - 1
     need = paged_attn_decode_prefix_workspace_bytes(B, Hq, desc.num_kv_heads, D, max_context_len, max_prefix_tokens,
                                                     desc.dtype)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pkv_paged_attn_decode_prefix(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_tables),
@@ -309,9 +336,10 @@ def paged_attn_decode_append(out, q, new_key, new_value, k_cache, v_cache, block
         raise ValueError("block_tables must be contiguous [B, max_blocks_per_seq]")
     if context_lens.numel() != B or not context_lens.is_contiguous():
         raise ValueError("context_lens must be contiguous [B]")
+    _on_device(q.device, block_tables, context_lens)
     need = paged_attn_workspace_bytes(B, Hq, desc.num_kv_heads, D, max_context_len, partition_size, desc.dtype)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pkv_paged_attn_decode_append(
         _ptr(out), _ptr(q), _ptr(new_key), _ptr(new_value), _ptr(k_cache), _ptr(v_cache),

@@ -35,12 +35,18 @@ class PagedKVCache:
             self.v_cache = torch.full(shape, fill, **mk)
         self.block_size = block_size
         self.device = device
+        self.pinned = pinned
+
+    def _device_pools(self, what: str) -> None:
+        if self.pinned:
+            raise ValueError(f"{what}: a pinned host cache is a swap space; sequences enter it with move_to")
 
     # -------------------------------------------------------------------- writing
     def write(self, slots, key, value, chunk_tokens: int = 1 << 15) -> None:
         """Scatter rows key/value [T, Hkv, D] to int64 ``slots`` through the append kernel."""
         import torch
 
+        self._device_pools("write")
         slots = torch.as_tensor(np.ascontiguousarray(slots, dtype=np.int64))
         T = int(slots.numel())
         for a in range(0, T, chunk_tokens):
@@ -57,6 +63,7 @@ class PagedKVCache:
         pairs = list(pairs)
         if not pairs:
             return
+        self._device_pools("copy_blocks")
         t = torch.tensor(pairs, dtype=torch.int32).reshape(-1, 2).to(self.device)
         binding.copy_blocks(self.k_cache, self.v_cache, t)
 

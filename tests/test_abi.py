@@ -399,3 +399,29 @@ def test_block_copies_reject_before_launch():
     assert lib.pkv_swap_blocks(None, 32, 4, 48, 64, 4, ctypes.byref(d), 16, 1, None) == 1
     assert lib.pkv_swap_blocks(16, 40, 4, 48, 64, 4, ctypes.byref(d), 16, 1, None) == 1  # misaligned
     assert lib.pkv_swap_blocks(16, 32, 4, 48, 64, 4, None, 16, 1, None) == 1
+
+
+def test_binding_refuses_index_arrays_off_the_launch_device():
+    """Tables, lengths, slots, pairs and group arrays on another device than the pools are
+    refused by the binding before any library call (a host pointer must not reach a kernel)."""
+    import torch
+
+    k = torch.zeros((4, 16, 2, 64), dtype=torch.bfloat16)
+    q = torch.zeros((2, 4, 64), dtype=torch.bfloat16)
+    out = torch.zeros_like(q)
+    bt_meta = torch.empty((2, 3), dtype=torch.int32, device="meta")
+    ctx = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="not on"):
+        B.paged_attn_decode(out, q, k, k.clone(), bt_meta, ctx, 40, 0.125)
+    with pytest.raises(ValueError, match="not on"):
+        B.paged_attn_decode_append(out, q, torch.zeros((2, 2, 64), dtype=torch.bfloat16),
+                                   torch.zeros((2, 2, 64), dtype=torch.bfloat16), k, k.clone(), bt_meta, ctx, 40, 0.125)
+    with pytest.raises(ValueError, match="not on"):
+        B.kv_cache_append(torch.zeros((3, 2, 64), dtype=torch.bfloat16), torch.zeros((3, 2, 64), dtype=torch.bfloat16),
+                          k, k.clone(), torch.empty(3, dtype=torch.int64, device="meta"))
+    with pytest.raises(ValueError, match="not on"):
+        B.copy_blocks(k, k.clone(), torch.empty((2, 2), dtype=torch.int32, device="meta"))
+    grp = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="not on"):
+        B.paged_attn_decode_prefix(out, q, k, k.clone(), torch.zeros((2, 3), dtype=torch.int32), ctx, 40, 0.125,
+                                   grp, torch.zeros(1, dtype=torch.int32, device="meta"), grp, 0)
