@@ -54,7 +54,8 @@ typedef enum {
   PKV_ERR_NOT_FOUND = 4,          /* unknown sequence id                                 */
   PKV_ERR_WORKSPACE_TOO_SMALL = 5,
   PKV_ERR_HIP = 6,                /* the HIP runtime refused a launch                    */
-  PKV_ERR_ALREADY_EXISTS = 7      /* sequence id already in use                          */
+  PKV_ERR_ALREADY_EXISTS = 7,     /* sequence id already in use                          */
+  PKV_ERR_HOST_MEMORY = 8         /* a host allocation failed (the pool is left unchanged) */
 } pkv_status;
 
 typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
@@ -337,7 +338,8 @@ PKV_API pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int32_t dst_num_blo
  * of physical block ids, a reference count per block ([gtnt] §2.1) and one block table per
  * sequence.  Pure host code.  Every operation is all-or-nothing: when the free list
  * cannot cover it (the admission check of the scheduler in [111cn] §2.2), it returns
- * PKV_ERR_OUT_OF_BLOCKS and nothing changes. */
+ * PKV_ERR_OUT_OF_BLOCKS and nothing changes; when a host allocation fails, it returns
+ * PKV_ERR_HOST_MEMORY and nothing changes either (no C++ exception leaves the library). */
 typedef struct pkv_block_pool pkv_block_pool;
 
 /* free_order: NULL for 0..num_blocks-1, else a permutation of 0..num_blocks-1; blocks are

@@ -21,7 +21,7 @@ OK = 0
 STATUS_NAMES = {
     0: "PKV_OK", 1: "PKV_ERR_INVALID_ARGUMENT", 2: "PKV_ERR_UNSUPPORTED",
     3: "PKV_ERR_OUT_OF_BLOCKS", 4: "PKV_ERR_NOT_FOUND", 5: "PKV_ERR_WORKSPACE_TOO_SMALL",
-    6: "PKV_ERR_HIP", 7: "PKV_ERR_ALREADY_EXISTS",
+    6: "PKV_ERR_HIP", 7: "PKV_ERR_ALREADY_EXISTS", 8: "PKV_ERR_HOST_MEMORY",
 }
 DTYPE_CODES = {"float32": 0, "float16": 1, "bfloat16": 2}
 

@@ -10,10 +10,14 @@
 // "PagedAttention分页注意力机制原理".
 //
 // Every mutating call first computes how many blocks it needs and fails with
-// PKV_ERR_OUT_OF_BLOCKS before touching anything if the free list is too short.
+// PKV_ERR_OUT_OF_BLOCKS before touching anything if the free list is too short.  Each also
+// makes every host allocation it needs before its first change to the pool, so that a failed
+// allocation (PKV_ERR_HOST_MEMORY; no exception crosses the C ABI) leaves the pool unchanged.
 #include <algorithm>
 #include <cstring>
+#include <memory>
 #include <new>
+#include <stdexcept>
 #include <unordered_map>
 #include <unordered_set>
 #include <vector>
@@ -36,6 +40,19 @@ namespace {
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Runs the body of an entry point; a host allocation that fails inside it becomes
+// PKV_ERR_HOST_MEMORY.
+template <typename F>
+pkv_status host_call(F&& body) {
+  try {
+    return body();
+  } catch (const std::bad_alloc&) {
+    return pkv::fail(PKV_ERR_HOST_MEMORY, "host allocation failed");
+  } catch (const std::length_error&) {
+    return pkv::fail(PKV_ERR_HOST_MEMORY, "host allocation too large");
+  }
+}
+
 // Blocks that appending n tokens to `s` takes from the free list (incl. a CoW copy).
 int64_t blocks_needed(const pkv_block_pool* p, const pkv_block_pool::Seq& s, int64_t n) {
   const int64_t bs = p->block_size;
@@ -53,30 +70,29 @@ extern "C" pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size,
   *out = nullptr;
   if (num_blocks <= 0) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "num_blocks=%d", num_blocks);
   if (block_size <= 0) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "block_size=%d", block_size);
-  pkv_block_pool* p = new (std::nothrow) pkv_block_pool();
-  if (!p) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "host allocation failed");
-  p->num_blocks = num_blocks;
-  p->block_size = block_size;
-  p->ref.assign(num_blocks, 0);
-  p->free_list.resize(num_blocks);
-  if (free_order) {
-    std::vector<char> seen(num_blocks, 0);
-    for (int32_t i = 0; i < num_blocks; ++i) {
-      int32_t b = free_order[i];
-      if (b < 0 || b >= num_blocks || seen[b]) {
-        delete p;
-        return pkv::fail(PKV_ERR_INVALID_ARGUMENT,
-                         "free_order is not a permutation of 0..%d (entry %d = %d)",
-                         num_blocks - 1, i, b);
+  return host_call([&]() -> pkv_status {
+    std::unique_ptr<pkv_block_pool> p(new pkv_block_pool());
+    p->num_blocks = num_blocks;
+    p->block_size = block_size;
+    p->ref.assign(num_blocks, 0);
+    p->free_list.resize(num_blocks);  // its capacity never drops below num_blocks: frees do not allocate
+    if (free_order) {
+      std::vector<char> seen(num_blocks, 0);
+      for (int32_t i = 0; i < num_blocks; ++i) {
+        int32_t b = free_order[i];
+        if (b < 0 || b >= num_blocks || seen[b])
+          return pkv::fail(PKV_ERR_INVALID_ARGUMENT,
+                           "free_order is not a permutation of 0..%d (entry %d = %d)",
+                           num_blocks - 1, i, b);
+        seen[b] = 1;
+        p->free_list[i] = b;
       }
-      seen[b] = 1;
-      p->free_list[i] = b;
+    } else {
+      for (int32_t i = 0; i < num_blocks; ++i) p->free_list[i] = i;
     }
-  } else {
-    for (int32_t i = 0; i < num_blocks; ++i) p->free_list[i] = i;
-  }
-  *out = p;
-  return PKV_OK;
+    *out = p.release();
+    return PKV_OK;
+  });
 }
 
 extern "C" void pkv_pool_destroy(pkv_block_pool* pool) { delete pool; }
@@ -115,18 +131,21 @@ extern "C" pkv_status pkv_seq_allocate(pkv_block_pool* p, int64_t seq, int32_t n
   if (need > static_cast<int64_t>(p->free_list.size()))
     return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "allocate needs %lld blocks, %zu free",
                      (long long)need, p->free_list.size());
-  pkv_block_pool::Seq s;
-  s.table.reserve(need);
-  for (int64_t i = 0; i < need; ++i) {
-    const int32_t b = p->free_list.back();
-    p->free_list.pop_back();
-    p->ref[b] = 1;
-    s.table.push_back(b);
-    if (blocks_out) blocks_out[i] = b;
-  }
-  s.num_tokens = num_tokens;
-  p->seqs.emplace(seq, std::move(s));
-  return PKV_OK;
+  return host_call([&]() -> pkv_status {
+    pkv_block_pool::Seq fresh;
+    fresh.table.reserve(need);
+    pkv_block_pool::Seq& s = p->seqs.emplace(seq, std::move(fresh)).first->second;
+    // no allocation from here on
+    for (int64_t i = 0; i < need; ++i) {
+      const int32_t b = p->free_list.back();
+      p->free_list.pop_back();
+      p->ref[b] = 1;
+      s.table.push_back(b);
+      if (blocks_out) blocks_out[i] = b;
+    }
+    s.num_tokens = num_tokens;
+    return PKV_OK;
+  });
 }
 
 extern "C" pkv_status pkv_seq_extend(pkv_block_pool* p, int64_t seq, int32_t n, int64_t* slots_out,
@@ -142,6 +161,11 @@ extern "C" pkv_status pkv_seq_extend(pkv_block_pool* p, int64_t seq, int32_t n, 
   if (need > static_cast<int64_t>(p->free_list.size()))
     return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "extend by %d needs %lld blocks, %zu free", n,
                      (long long)need, p->free_list.size());
+  try {
+    s.table.reserve(s.table.size() + need);  // the loop below then allocates nothing
+  } catch (const std::exception&) {
+    return pkv::fail(PKV_ERR_HOST_MEMORY, "host allocation failed");
+  }
   const int64_t bs = p->block_size;
   for (int32_t i = 0; i < n; ++i) {
     const int64_t offset = s.num_tokens % bs;
@@ -175,10 +199,12 @@ extern "C" pkv_status pkv_seq_fork(pkv_block_pool* p, int64_t parent, int64_t ch
   auto it = p->seqs.find(parent);
   if (it == p->seqs.end()) return pkv::fail(PKV_ERR_NOT_FOUND, "sequence %lld", (long long)parent);
   if (p->seqs.count(child)) return pkv::fail(PKV_ERR_ALREADY_EXISTS, "sequence %lld exists", (long long)child);
-  pkv_block_pool::Seq c = it->second;  // copy: table and token count
-  for (int32_t b : c.table) p->ref[b] += 1;
-  p->seqs.emplace(child, std::move(c));
-  return PKV_OK;
+  return host_call([&]() -> pkv_status {
+    pkv_block_pool::Seq c = it->second;  // copy: table and token count
+    const pkv_block_pool::Seq& added = p->seqs.emplace(child, std::move(c)).first->second;
+    for (int32_t b : added.table) p->ref[b] += 1;
+    return PKV_OK;
+  });
 }
 
 extern "C" pkv_status pkv_seq_free(pkv_block_pool* p, int64_t seq) {
@@ -245,52 +271,60 @@ extern "C" pkv_status pkv_pool_move_seqs(pkv_block_pool* src, pkv_block_pool* ds
     return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "block sizes differ (%d, %d)", src->block_size, dst->block_size);
   if (n < 0 || (n > 0 && !seqs)) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "n=%d seqs=%p", n, (const void*)seqs);
   if (capacity < 0) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "capacity=%d", capacity);
-  // validate everything before changing anything
-  std::unordered_set<int64_t> seen;
-  std::unordered_map<int32_t, int32_t> uses;  // block -> references held by the moving sequences
-  std::vector<int32_t> order;                  // distinct blocks, first use first
-  for (int32_t i = 0; i < n; ++i) {
-    auto it = src->seqs.find(seqs[i]);
-    if (it == src->seqs.end()) return pkv::fail(PKV_ERR_NOT_FOUND, "sequence %lld", (long long)seqs[i]);
-    if (dst->seqs.count(seqs[i]))
-      return pkv::fail(PKV_ERR_ALREADY_EXISTS, "sequence %lld exists in the destination", (long long)seqs[i]);
-    if (!seen.insert(seqs[i]).second)
-      return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "sequence %lld listed twice", (long long)seqs[i]);
-    for (int32_t b : it->second.table)
-      if (uses[b]++ == 0) order.push_back(b);
-  }
-  for (int32_t b : order)
-    if (src->ref[b] != uses[b])
-      return pkv::fail(PKV_ERR_UNSUPPORTED, "block %d is also used by a sequence that does not move", b);
-  if (order.size() > dst->free_list.size())
-    return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "need %zu blocks, %zu free", order.size(), dst->free_list.size());
-  if (static_cast<int64_t>(order.size()) > capacity || (!pairs_out && !order.empty()))
-    return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "pairs_out holds %d pairs, %zu needed", pairs_out ? capacity : 0,
-                     order.size());
-  std::unordered_map<int32_t, int32_t> to;
-  for (size_t k = 0; k < order.size(); ++k) {
-    const int32_t b = order[k];
-    const int32_t nb = dst->free_list.back();
-    dst->free_list.pop_back();
-    dst->ref[nb] = uses[b];
-    to[b] = nb;
-    pairs_out[2 * k] = b;
-    pairs_out[2 * k + 1] = nb;
-  }
-  for (int32_t i = 0; i < n; ++i) {
-    auto it = src->seqs.find(seqs[i]);
-    pkv_block_pool::Seq moved;
-    moved.num_tokens = it->second.num_tokens;
-    moved.table.reserve(it->second.table.size());
-    for (int32_t b : it->second.table) {
-      moved.table.push_back(to[b]);
-      if (--src->ref[b] == 0) src->free_list.push_back(b);
+  return host_call([&]() -> pkv_status {
+    // validate everything, and make every allocation, before changing anything
+    std::unordered_set<int64_t> seen;
+    std::unordered_map<int32_t, int32_t> uses;  // block -> references held by the moving sequences
+    std::vector<int32_t> order;                  // distinct blocks, first use first
+    for (int32_t i = 0; i < n; ++i) {
+      auto it = src->seqs.find(seqs[i]);
+      if (it == src->seqs.end()) return pkv::fail(PKV_ERR_NOT_FOUND, "sequence %lld", (long long)seqs[i]);
+      if (dst->seqs.count(seqs[i]))
+        return pkv::fail(PKV_ERR_ALREADY_EXISTS, "sequence %lld exists in the destination", (long long)seqs[i]);
+      if (!seen.insert(seqs[i]).second)
+        return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "sequence %lld listed twice", (long long)seqs[i]);
+      for (int32_t b : it->second.table)
+        if (uses[b]++ == 0) order.push_back(b);
     }
-    src->seqs.erase(it);
-    dst->seqs.emplace(seqs[i], std::move(moved));
-  }
-  if (num_pairs_out) *num_pairs_out = static_cast<int32_t>(order.size());
-  return PKV_OK;
+    for (int32_t b : order)
+      if (src->ref[b] != uses[b])
+        return pkv::fail(PKV_ERR_UNSUPPORTED, "block %d is also used by a sequence that does not move", b);
+    if (order.size() > dst->free_list.size())
+      return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "need %zu blocks, %zu free", order.size(), dst->free_list.size());
+    if (static_cast<int64_t>(order.size()) > capacity || (!pairs_out && !order.empty()))
+      return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "pairs_out holds %d pairs, %zu needed", pairs_out ? capacity : 0,
+                       order.size());
+    // block k of `order` takes the k-th block from the end of dst's free list
+    std::unordered_map<int32_t, int32_t> to;
+    to.reserve(order.size());
+    const size_t nfree = dst->free_list.size();
+    for (size_t k = 0; k < order.size(); ++k) to.emplace(order[k], dst->free_list[nfree - 1 - k]);
+    std::vector<std::vector<int32_t>> tables(n);
+    for (int32_t i = 0; i < n; ++i) {
+      const std::vector<int32_t>& t = src->seqs.find(seqs[i])->second.table;
+      tables[i].reserve(t.size());
+      for (int32_t b : t) tables[i].push_back(to.find(b)->second);
+    }
+    dst->seqs.reserve(dst->seqs.size() + n);  // the node moves below then never rehash
+    // changes: no allocation from here on
+    for (size_t k = 0; k < order.size(); ++k) {
+      const int32_t b = order[k];
+      const int32_t nb = dst->free_list.back();
+      dst->free_list.pop_back();
+      dst->ref[nb] = uses.find(b)->second;
+      pairs_out[2 * k] = b;
+      pairs_out[2 * k + 1] = nb;
+    }
+    for (int32_t i = 0; i < n; ++i) {
+      auto node = src->seqs.extract(seqs[i]);
+      for (int32_t b : node.mapped().table)
+        if (--src->ref[b] == 0) src->free_list.push_back(b);
+      node.mapped().table = std::move(tables[i]);
+      dst->seqs.insert(std::move(node));
+    }
+    if (num_pairs_out) *num_pairs_out = static_cast<int32_t>(order.size());
+    return PKV_OK;
+  });
 }
 
 // Groups of batch entries whose contexts start with the same physical blocks (prefix sharing
@@ -309,49 +343,51 @@ extern "C" pkv_status pkv_pool_prefix_groups(const pkv_block_pool* p, const int6
   if (min_prefix_tokens < 0) return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "min_prefix_tokens=%d", min_prefix_tokens);
   if (!seq_prefix_out || !group_offsets_out || !group_members_out || !num_groups_out || !max_prefix_out)
     return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "NULL output");
-  std::vector<const pkv_block_pool::Seq*> rows(n);
-  for (int32_t i = 0; i < n; ++i) {
-    auto it = p->seqs.find(seqs[i]);
-    if (it == p->seqs.end()) return pkv::fail(PKV_ERR_NOT_FOUND, "sequence %lld", (long long)seqs[i]);
-    rows[i] = &it->second;
-  }
-  const int64_t bs = p->block_size;
-  std::unordered_map<int32_t, std::vector<int32_t>> bucket;
-  std::vector<int32_t> first_seen;  // first blocks in order of first appearance
-  for (int32_t i = 0; i < n; ++i) {
-    seq_prefix_out[i] = 0;
-    if (rows[i]->num_tokens / bs < 1) continue;  // no full block
-    const int32_t b0 = rows[i]->table[0];
-    auto& v = bucket[b0];
-    if (v.empty()) first_seen.push_back(b0);
-    v.push_back(i);
-  }
-  int32_t ng = 0, off = 0, maxp = 0;
-  for (int32_t b0 : first_seen) {
-    const std::vector<int32_t>& mem = bucket[b0];
-    if (mem.size() < 2) continue;
-    int64_t K = INT64_MAX;
-    for (int32_t i : mem) K = std::min<int64_t>(K, rows[i]->num_tokens / bs);
-    const std::vector<int32_t>& lead = rows[mem[0]]->table;
-    for (int64_t k = 1; k < K; ++k) {
-      bool same = true;
-      for (int32_t i : mem) same = same && rows[i]->table[k] == lead[k];
-      if (!same) {
-        K = k;
-        break;
+  return host_call([&]() -> pkv_status {
+    std::vector<const pkv_block_pool::Seq*> rows(n);
+    for (int32_t i = 0; i < n; ++i) {
+      auto it = p->seqs.find(seqs[i]);
+      if (it == p->seqs.end()) return pkv::fail(PKV_ERR_NOT_FOUND, "sequence %lld", (long long)seqs[i]);
+      rows[i] = &it->second;
+    }
+    const int64_t bs = p->block_size;
+    std::unordered_map<int32_t, std::vector<int32_t>> bucket;
+    std::vector<int32_t> first_seen;  // first blocks in order of first appearance
+    for (int32_t i = 0; i < n; ++i) {
+      seq_prefix_out[i] = 0;
+      if (rows[i]->num_tokens / bs < 1) continue;  // no full block
+      const int32_t b0 = rows[i]->table[0];
+      auto& v = bucket[b0];
+      if (v.empty()) first_seen.push_back(b0);
+      v.push_back(i);
+    }
+    int32_t ng = 0, off = 0, maxp = 0;
+    for (int32_t b0 : first_seen) {
+      const std::vector<int32_t>& mem = bucket[b0];
+      if (mem.size() < 2) continue;
+      int64_t K = INT64_MAX;
+      for (int32_t i : mem) K = std::min<int64_t>(K, rows[i]->num_tokens / bs);
+      const std::vector<int32_t>& lead = rows[mem[0]]->table;
+      for (int64_t k = 1; k < K; ++k) {
+        bool same = true;
+        for (int32_t i : mem) same = same && rows[i]->table[k] == lead[k];
+        if (!same) {
+          K = k;
+          break;
+        }
       }
+      const int64_t P = K * bs / 16 * 16;
+      if (P < std::max<int64_t>(16, min_prefix_tokens) || P > INT32_MAX) continue;
+      group_offsets_out[ng++] = off;
+      for (int32_t i : mem) {
+        group_members_out[off++] = i;
+        seq_prefix_out[i] = static_cast<int32_t>(P);
+      }
+      maxp = std::max<int32_t>(maxp, static_cast<int32_t>(P));
     }
-    const int64_t P = K * bs / 16 * 16;
-    if (P < std::max<int64_t>(16, min_prefix_tokens) || P > INT32_MAX) continue;
-    group_offsets_out[ng++] = off;
-    for (int32_t i : mem) {
-      group_members_out[off++] = i;
-      seq_prefix_out[i] = static_cast<int32_t>(P);
-    }
-    maxp = std::max<int32_t>(maxp, static_cast<int32_t>(P));
-  }
-  group_offsets_out[ng] = off;
-  *num_groups_out = ng;
-  *max_prefix_out = maxp;
-  return PKV_OK;
+    group_offsets_out[ng] = off;
+    *num_groups_out = ng;
+    *max_prefix_out = maxp;
+    return PKV_OK;
+  });
 }

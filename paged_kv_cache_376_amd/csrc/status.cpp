@@ -16,7 +16,10 @@ pkv_status fail(pkv_status s, const char* fmt, ...) {
   va_start(ap, fmt);
   std::vsnprintf(buf, sizeof(buf), fmt, ap);
   va_end(ap);
-  g_last_error = std::string(pkv_status_string(s)) + ": " + buf;
+  try {
+    g_last_error = std::string(pkv_status_string(s)) + ": " + buf;
+  } catch (...) {  // no host memory even for the message: keep the status, drop the text
+  }
   return s;
 }
 
@@ -36,6 +39,7 @@ extern "C" const char* pkv_status_string(int32_t status) {
     case PKV_ERR_WORKSPACE_TOO_SMALL: return "PKV_ERR_WORKSPACE_TOO_SMALL";
     case PKV_ERR_HIP: return "PKV_ERR_HIP";
     case PKV_ERR_ALREADY_EXISTS: return "PKV_ERR_ALREADY_EXISTS";
+    case PKV_ERR_HOST_MEMORY: return "PKV_ERR_HOST_MEMORY";
     default: return "PKV_ERR_UNKNOWN";
   }
 }

@@ -37,6 +37,10 @@ def test_version_and_status_strings():
     lib = B.lib()
     assert lib.pkv_status_string(3) == b"PKV_ERR_OUT_OF_BLOCKS"
     assert lib.pkv_status_string(99) == b"PKV_ERR_UNKNOWN"
+    # every status the header declares has its name, and the binding agrees
+    for code, name in B.STATUS_NAMES.items():
+        assert lib.pkv_status_string(code) == name.encode()
+    assert B.STATUS_NAMES[8] == "PKV_ERR_HOST_MEMORY"
 
 
 # ------------------------------------------------------------------ host pool vs oracle
