@@ -1,0 +1,137 @@
+"""GPU: the library's calls captured into HIP graphs (torch.cuda.CUDAGraph on ROCm) and
+replayed.  Each replay, with the program's own eager work and synchronisations between
+replays, must give bit for bit the eager result: the calls record no memset nodes and keep
+no state between launches beyond their arguments."""
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_376_amd import binding
+from paged_kv_cache_376_amd import workloads as W
+from paged_kv_cache_376_amd.cache import build_cache
+from tests.gpu_common import DEVICE, TOL, bits, max_err, oracle_out, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _eager_noise():
+    x = torch.randn(1 << 20, device=DEVICE)
+    y = (x * 2).sum()
+    torch.cuda.synchronize()
+    return y
+
+
+def _replay_and_check(graph, out, expect, replays=4):
+    for i in range(replays):
+        out.fill_(float("nan"))
+        _eager_noise()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(out.cpu()), bits(expect)), f"replay {i}"
+
+
+@pytest.mark.parametrize("name", ["gqa_bf16", "mha_fp16"])
+def test_fused_decode_step_in_a_graph(name):
+    say(f"[graph] fused decode step {name}")
+    overrides = {"gqa_bf16": {"num_seqs": 24, "len_hi": 2000}, "mha_fp16": {"num_seqs": 8, "len_hi": 900}}[name]
+    w = W.make_workload(name, 3, **overrides)
+    cache = build_cache(w, DEVICE, fill=float("nan"))
+    seqs = list(range(w.spec.num_seqs))
+    for s in seqs:
+        _, cow = cache.pool.seq_extend(s, 1)
+        cache.copy_blocks(cow)
+    bt, ctx, maxc = cache.tables(seqs)
+    q = w.q.to(DEVICE)
+    nk, nv = w.new_k.to(DEVICE), w.new_v.to(DEVICE)
+    sp = w.spec
+    ws = torch.empty(binding.paged_attn_workspace_bytes(sp.num_seqs, sp.num_q_heads, sp.num_kv_heads, sp.head_dim,
+                                                        maxc, 0, sp.dtype), dtype=torch.uint8, device=DEVICE)
+    out = torch.empty_like(q)
+    call = lambda: binding.paged_attn_decode_append(out, q, nk, nv, cache.k_cache, cache.v_cache, bt, ctx, maxc,
+                                                    w.scale, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    expect = out.cpu()
+    assert max_err(expect, oracle_out(w)) <= TOL[sp.dtype]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    _replay_and_check(g, out, expect)
+
+
+def test_prefix_decode_in_a_graph():
+    say("[graph] prefix-shared decode")
+    w = W.Workload(W.SPECS["prefix_bf16"].replace(num_seqs=16, suffix_hi=200), seed=4)
+    cache = build_cache(w, DEVICE, fill=float("nan"))
+    seqs = list(range(w.spec.num_seqs))
+    cache.append_tokens(seqs, w.new_k, w.new_v)
+    bt, ctx, maxc = cache.tables(seqs)
+    spf, offs, mem, mx = cache.pool.prefix_groups(seqs)
+    d32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEVICE)
+    spd, offd, memd = d32(spf), d32(offs), d32(mem)
+    sp = w.spec
+    ws = torch.empty(binding.paged_attn_decode_prefix_workspace_bytes(sp.num_seqs, sp.num_q_heads, sp.num_kv_heads,
+                                                                      sp.head_dim, maxc, mx, sp.dtype),
+                     dtype=torch.uint8, device=DEVICE)
+    q = w.q.to(DEVICE)
+    out = torch.empty_like(q)
+    call = lambda: binding.paged_attn_decode_prefix(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale,
+                                                    spd, offd, memd, mx, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    expect = out.cpu()
+    assert max_err(expect, oracle_out(w)) <= TOL["bfloat16"]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    _replay_and_check(g, out, expect)
+
+
+def test_append_and_copy_in_a_graph():
+    """A copy-on-write block copy followed by the append of rows into the copies, captured
+    once: every replay leaves the pools bit for bit as the eager calls did."""
+    say("[graph] copy_blocks + append")
+    rng = np.random.default_rng(5)
+    nb, shape = 64, (16, 8, 128)
+    k0 = torch.from_numpy(rng.standard_normal((nb,) + shape, dtype=np.float32)).to(torch.bfloat16).to(DEVICE)
+    v0 = torch.from_numpy(rng.standard_normal((nb,) + shape, dtype=np.float32)).to(torch.bfloat16).to(DEVICE)
+    k, v = k0.clone(), v0.clone()
+    perm = rng.permutation(nb)
+    pairs = torch.from_numpy(np.stack([perm[:10], perm[10:20]], axis=1).astype(np.int32)).to(DEVICE)
+    slots = torch.from_numpy((perm[10:20].astype(np.int64) * 16 + rng.integers(0, 16, size=10))).to(DEVICE)
+    rows_k = torch.from_numpy(rng.standard_normal((10, 8, 128), dtype=np.float32)).to(torch.bfloat16).to(DEVICE)
+    rows_v = torch.from_numpy(rng.standard_normal((10, 8, 128), dtype=np.float32)).to(torch.bfloat16).to(DEVICE)
+
+    def call():
+        binding.copy_blocks(k, v, pairs)
+        binding.kv_cache_append(rows_k, rows_v, k, v, slots)
+
+    call()
+    torch.cuda.synchronize()
+    ek, ev = k.cpu(), v.cpu()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i in range(3):
+        k.copy_(k0)
+        v.copy_(v0)
+        _eager_noise()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(k.cpu()), bits(ek)) and torch.equal(bits(v.cpu()), bits(ev)), f"replay {i}"
