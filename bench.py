@@ -153,6 +153,40 @@ def _time_calls(fn, steps, warmup, stream):
     return a.elapsed_time(b) / steps / 1e3  # seconds per call
 
 
+def read_ceiling(dev):
+    """The device's practical HBM read ceiling: a plain contiguous read of 1 GiB (16-byte
+    loads, 8 in flight per thread, 2048 work-groups) by the probe library the build makes
+    next to libpagedkv, timed with HIP events on the launch stream.  None when the probe
+    library is missing."""
+    import ctypes
+
+    import torch
+
+    from paged_kv_cache_376_amd import build as pkv_build
+
+    if not os.path.exists(pkv_build.PROBE_PATH):
+        return None
+    probe = ctypes.CDLL(pkv_build.PROBE_PATH)
+    fn = probe.pkv_read_ceiling_pass
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(2048, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def one():
+        rc = fn(buf.data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"read-ceiling probe launch failed ({rc})")
+
+    t = _time_calls(one, 20, 3, stream)
+    del buf
+    gbs = nbytes / t / 1e9
+    return {"value": round(gbs, 1), "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "probe": "contiguous read of 1 GiB, 16-byte loads, 8 in flight per thread, 2048 work-groups of 256"}
+
+
 def bench_copy_blocks(args, dev):
     """pkv_copy_blocks on the default workload's block shape: 4096 (source, destination)
     pairs drawn from a 16384-block pool per call; bytes = pairs x 2 pools x block x (read +
@@ -497,6 +531,12 @@ def main():
             "avg_launch_us": round(dec_s * 1e6, 2),
         },
     }
+    ceiling = read_ceiling(dev)
+    if ceiling is not None:
+        log(f"practical read ceiling of this device: {ceiling['value']:.0f} GB/s "
+            f"({100 * ceiling['frac_of_peak']:.1f}% of {HBM_PEAK_GBS:.0f})")
+        result["read_ceiling"] = ceiling
+        result["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["value"], 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
