@@ -343,6 +343,10 @@ def test_workspace_size_and_partition_rules():
     assert w128 > 0 and w128 % per_range128 == 0 and w64 % per_range64 == 0
     assert w128 // per_range128 == w64 // per_range64  # same number of ranges
     assert ws(256, 64, 8, 128, 8192, 0) == w128  # deterministic
+    # small batches: one range per 8 worst-case tiles (4 x 1024 tokens: 256 tiles -> 32 ranges),
+    # large ones: about 2048 waves (8 per work-group, 4 KV heads each -> 128 ranges at 8 KV heads)
+    assert ws(4, 64, 8, 128, 1024, 0) == 32 * per_range128
+    assert ws(256, 64, 8, 128, 8192, 0) == 128 * per_range128
     # tiny contexts: at most one range per 8 worst-case tiles
     assert ws(1, 8, 1, 128, 16, 0) <= 2 * rec128 + 256
     assert ws(0, 64, 8, 128, 8192, 0) == 0
