@@ -341,7 +341,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        sys.exit("bench.py measures one GPU only: this build has no multi-GPU path "
+        sys.exit("bench.py measures one GPU only: the library has no multi-GPU path "
                  "(decode attention shards by KV head or sequence with no exchange; see the "
                  "design notes). Run with --gpus 1.")
 
