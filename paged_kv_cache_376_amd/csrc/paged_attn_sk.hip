@@ -588,6 +588,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
 #pragma unroll
     for (int q = 0; q < NC; ++q) x[q] = *reinterpret_cast<const f32x4*>(p.ws_acc + rec * (16 * D) + hr * D + 16 * q + 4 * grp);
   };
+  // The same through buffer resources: a record that is not needed (valid false) is a
+  // zero-length load, which touches no memory, so a batch never loads one record twice.
+  auto load_rec_if = [&](int64_t rec, bool valid, float2& ml, f32x4* x) {
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.ws_acc) + rec * (16 * D), 0, valid ? 16 * D * 4 : 0, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.ws_ml) + rec * 32, 0, valid ? 32 * 4 : 0, kRsrcWord3);
+    ml = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rm, hr * 8, 0, 0));
+#pragma unroll
+    for (int q = 0; q < NC; ++q)
+      x[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (hr * D + 16 * q + 4 * grp) * 4, 0, 0));
+  };
   extern __shared__ __attribute__((aligned(16))) unsigned char s_merge[];
   f32x4* s_a = reinterpret_cast<f32x4*>(s_merge + hw * (NC * 64 * 16 + 64 * 8));
   float2* s_ml = reinterpret_cast<float2*>(s_merge + hw * (NC * 64 * 16 + 64 * 8) + NC * 64 * 16);
@@ -615,7 +627,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
       float2 ml[U];
       f32x4 x[U][NC];
 #pragma unroll
-      for (int u = 0; u < U; ++u) load_rec(rec_of(c0 + u <= rb ? c0 + u : c0, 0), ml[u], x[u]);
+      for (int u = 0; u < U; ++u) load_rec_if(rec_of(c0 + u <= rb ? c0 + u : c0, 0), c0 + u <= rb, ml[u], x[u]);
       __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the first use
       fold_records<U, NC>(m, l, a, ml, x, rb - c0 + 1);
     }
