@@ -501,6 +501,8 @@ def main():
         "decode_tokens_per_s_70b_shape_attention_only": round(sp.num_seqs / (LAYERS_70B * ms_step / 1e3), 1),
         "append_us": None if t_app is None else round(float(t_app.mean()) * 1e3, 2),
         "decode_us_median": round(float(np.median(t_dec)) * 1e3, 2),
+        "decode_us_p10": round(float(np.percentile(t_dec, 10)) * 1e3, 2),
+        "decode_us_p90": round(float(np.percentile(t_dec, 90)) * 1e3, 2),
         "step_calls": "pkv_kv_cache_append + pkv_paged_attn_decode_prefix" if args.prefix_shared
                       else "pkv_kv_cache_append + pkv_paged_attn_decode" if args.separate
                       else "pkv_paged_attn_decode_append (append fused into the decode)",
