@@ -71,11 +71,17 @@ SK_SOURCES = [os.path.join(ROOT, "paged_kv_cache_376_amd", "csrc", f)
 
 
 def sk_source_sha256():
+    """SHA-256 of the decode and merge kernels' sources with comments and whitespace removed:
+    an edit of a comment does not change what the counters measured, an edit of code does."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for f in SK_SOURCES:
-        h.update(open(f, "rb").read())
+        text = open(f, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -2,22 +2,24 @@
 //
 // What is computed is the same as in paged_attn.hip: for every sequence and query head,
 // single-query scaled dot-product attention over the sequence's context, whose K/V rows sit
-// in 16-token blocks scattered through a pool and are found through the block table (the
-// yunthe.com page "大模型推理显存优化实战：PagedAttention机制原理与vLLM连续批处理配置",
-// section "PagedAttention分页注意力机制原理"; block table and 16-token blocks: the 111cn.net
-// page "大模型推理引擎高频优化：连续批处理、PagedAttention 与 KV Cache 实战拆解" §3.2; block
-// layout (block_size, heads, head_dim): the gtnt.cn page "vLLM推理加速框架：PagedAttention与
-// 连续批处理技术解析" §2.1).  This file only changes how the work is spread over the chip.
+// in fixed-size blocks (16 tokens, or 8 or 32) scattered through a pool and are found through
+// the block table (the yunthe.com page "大模型推理显存优化实战：PagedAttention机制原理与vLLM
+// 连续批处理配置", section "PagedAttention分页注意力机制原理"; block table and 16-token blocks:
+// the 111cn.net page "大模型推理引擎高频优化：连续批处理、PagedAttention 与 KV Cache 实战拆解"
+// §3.2; block layout (block_size, heads, head_dim): the gtnt.cn page "vLLM推理加速框架：
+// PagedAttention与连续批处理技术解析" §2.1; 8-token blocks: its closing section).  This file only
+// changes how the work is spread over the chip.
 //
-// Work split.  A "tile" is one 16-token block of one sequence for one KV head (K and V:
-// 2*16*D*e bytes).  For one KV head the tiles of all sequences form a list in sequence order
-// (block 0..nblk-1 of sequence 0, then sequence 1, ...), T tiles long; a sequence with no
-// context counts as one empty tile, so that its zero output is written like any other.  The
-// list is cut into R equal contiguous ranges (R never exceeds T, so no range is empty).  A
-// work-group serves one range for 4 consecutive KV heads, one head per wave column, so its
-// waves read neighbouring 256-byte slices of the same token rows at the same time; the range
-// is split again between 2 wave rows.  Every wave therefore streams the same number of tiles
-// (+-1) whatever the length mix, and keeps loading across sequence boundaries.
+// Work split.  A "tile" is 16 tokens of one sequence for one KV head (one 16-token block, half
+// of a 32-token block or two 8-token blocks; K and V: 2*16*D*e bytes).  For one KV head the
+// tiles of all sequences form a list in sequence order (tiles 0..n-1 of sequence 0, then
+// sequence 1, ...), T tiles long; a sequence with no context counts as one empty tile, so that
+// its zero output is written like any other.  The list is cut into R equal contiguous ranges
+// (R never exceeds T, so no range is empty).  A work-group serves one range for 4 consecutive
+// KV heads, one head per wave column, so its waves read neighbouring 256-byte slices of the
+// same token rows at the same time; the range is split again between 2 wave rows.  Every
+// wave therefore streams the same number of tiles (+-1) whatever the length mix, and keeps
+// loading across sequence boundaries.
 //   * A sequence whose tiles lie inside one wave's sub-range is finished by that wave.
 //   * A sequence cut only between the two sub-ranges of a work-group is merged in LDS.
 //   * A sequence cut by range boundaries leaves one record (unnormalised acc, running max m,
