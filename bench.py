@@ -172,13 +172,19 @@ def cpu_baseline(w, budget_s=15.0):
                   "sample": f"the same {len(small)} sequences ({b1 / 1e6:.1f} MB of K/V, {t1:.1f} s)"}
     finally:
         torch.set_num_threads(n_threads)
-    return {"value": round(float(np.median(runs)), 4), "unit": "GB/s", "cores": cores,
+    all_cores = {"value": round(float(np.median(runs)), 4), "unit": "GB/s", "cores": cores,
+                 "runs": [round(r, 4) for r in runs],
+                 "threads": f"torch {n_threads}, {', '.join(blas) or 'blas n/a'}"}
+    # the faster of the two configurations is the baseline (its per-sequence products are small
+    # enough that threaded BLAS can lose to one thread)
+    best = single if single is not None and single["value"] > all_cores["value"] else all_cores
+    return {"value": best["value"], "unit": "GB/s", "cores": best["cores"],
             "kind": "oracle",
             "sample": f"first {len(sample)} of {sp.num_seqs} sequences of the same workload "
                       f"({nbytes / 1e6:.1f} MB of K/V per pass), fp64 numpy, upcast inside the timer; "
-                      f"median of 3 timed passes after a warm-up; thread pools: torch {n_threads}, "
-                      f"{', '.join(blas) or 'blas n/a'}; host cores available {len(os.sched_getaffinity(0))}",
-            "runs": [round(r, 4) for r in runs],
+                      f"all cores: median of 3 timed passes after a warm-up; one thread: one pass; the "
+                      f"faster is reported; host cores available {len(os.sched_getaffinity(0))}",
+            "all_cores": all_cores,
             "single_thread": single,
             "cpu_model": _cpu_model(),
             "note": "the oracle is a correctness tool, not a tuned CPU kernel"}
