@@ -27,17 +27,29 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint4* __restrict_
                                                         const int64_t* __restrict__ slot_mapping,
                                                         int64_t num_slots, int32_t row_vecs) {
   const int64_t tok = blockIdx.x;
-  const int64_t slot = slot_mapping[tok];
-  if (slot < 0 || slot >= num_slots) return;
   const uint4* ks = key + tok * row_vecs;
   const uint4* vs = value + tok * row_vecs;
+  // the row's first piece is loaded together with its slot (they do not depend on each other),
+  // so that a short row costs one round trip
+  const int32_t i0 = threadIdx.x;
+  uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
+  if (i0 < row_vecs) {
+    a = ks[i0];
+    b = vs[i0];
+  }
+  const int64_t slot = slot_mapping[tok];
+  if (slot < 0 || slot >= num_slots) return;
   uint4* kd = k_cache + slot * row_vecs;
   uint4* vd = v_cache + slot * row_vecs;
-  for (int32_t i = threadIdx.x; i < row_vecs; i += blockDim.x) {
-    const uint4 a = ks[i];
-    const uint4 b = vs[i];
-    kd[i] = a;
-    vd[i] = b;
+  if (i0 < row_vecs) {
+    kd[i0] = a;
+    vd[i0] = b;
+  }
+  for (int32_t i = i0 + blockDim.x; i < row_vecs; i += blockDim.x) {
+    const uint4 c = ks[i];
+    const uint4 d = vs[i];
+    kd[i] = c;
+    vd[i] = d;
   }
 }
 
@@ -54,6 +66,15 @@ __global__ __launch_bounds__(256) void kv_append_last_kernel(const uint4* __rest
                                                              int32_t max_context_len, int32_t num_blocks,
                                                              int32_t block_size, int32_t row_vecs) {
   const int64_t s = blockIdx.x;
+  const uint4* ks = key + s * row_vecs;
+  const uint4* vs = value + s * row_vecs;
+  // the row's first piece is loaded while the context length and table entry are fetched
+  const int32_t i0 = threadIdx.x;
+  uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
+  if (i0 < row_vecs) {
+    a = ks[i0];
+    b = vs[i0];
+  }
   int ctx = context_lens[s];
   ctx = ctx > max_context_len ? max_context_len : ctx;
   if (ctx <= 0) return;
@@ -61,15 +82,17 @@ __global__ __launch_bounds__(256) void kv_append_last_kernel(const uint4* __rest
   const int phys = block_tables[s * max_blocks_per_seq + t / block_size];
   if (phys < 0 || phys >= num_blocks) return;
   const int64_t slot = static_cast<int64_t>(phys) * block_size + t % block_size;
-  const uint4* ks = key + s * row_vecs;
-  const uint4* vs = value + s * row_vecs;
   uint4* kd = k_cache + slot * row_vecs;
   uint4* vd = v_cache + slot * row_vecs;
-  for (int32_t i = threadIdx.x; i < row_vecs; i += blockDim.x) {
-    const uint4 a = ks[i];
-    const uint4 b = vs[i];
-    kd[i] = a;
-    vd[i] = b;
+  if (i0 < row_vecs) {
+    kd[i0] = a;
+    vd[i0] = b;
+  }
+  for (int32_t i = i0 + blockDim.x; i < row_vecs; i += blockDim.x) {
+    const uint4 c = ks[i];
+    const uint4 d = vs[i];
+    kd[i] = c;
+    vd[i] = d;
   }
 }
 
