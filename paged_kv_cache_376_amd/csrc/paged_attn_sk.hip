@@ -33,8 +33,9 @@
 //   running max grows by more than 8 (exact: the stale max only bounds P by 2^8)
 //   O^T += V^T * P^T         v_mfma_f32_16x16x16, V^T read from an LDS copy of the V tile with
 //                            ds_read_b64_tr_b16 (one transposing read per 16-column chunk)
-// Loads use buffer resources so that a slot past the end of the range is a zero-length load
-// (no memory access) and the pipeline stays unconditional.
+// Loads use buffer resources that end at the tile's last row in use: the rows of a partly
+// filled last tile past the context, and a tile whose block id lies outside the pool, read as
+// zeros with no memory access, so the loads need no branches around them.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -290,11 +291,15 @@ void decode_sk_kernel(SkParams p) {
 #pragma unroll
           for (int c = 0; c < KC; ++c) { nk[c] = kn[grp + 4 * c]; nv[c] = vn[grp + 4 * c]; }
         }
-        nrec = (phys >= 0 && phys < p.num_blocks) ? static_cast<int>((BS == 8 ? 8 : kTile) * tok_bytes) : 0;
-        phys = nrec ? phys : 0;
+        // Rows the tile takes from the pool: its tokens, less the new token of a fused append
+        // (that row comes from the input).  The resource ends after them, so the rows of a
+        // partly filled last tile past the context read as zeros and fetch nothing.
+        const int rows = max(0, (fl & 0xff) - ((append && (fl & kLast)) ? 1 : 0));
+        nrec = (phys >= 0 && phys < p.num_blocks) ? static_cast<int>(min(rows, BS == 8 ? 8 : kTile) * tok_bytes) : 0;
+        phys = (phys >= 0 && phys < p.num_blocks) ? phys : 0;
         if (BS == 32) half = (fl & kHalf) ? 1 : 0;
         if (BS == 8) {
-          nrec1 = (phys1 >= 0 && phys1 < p.num_blocks) ? static_cast<int>(kTile * tok_bytes) : 0;
+          nrec1 = (phys1 >= 0 && phys1 < p.num_blocks) ? static_cast<int>(rows * tok_bytes) : 0;
           phys1 = nrec1 ? phys1 : 0;
         }
       }
@@ -361,7 +366,9 @@ void decode_sk_kernel(SkParams p) {
       f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < KC; ++c) sacc = M::qk(__builtin_bit_cast(typename M::v8, kbuf[c]), qb[c], sacc);
-      issue(k + 1);  // this tile's registers are consumed: the next tile's loads go out now
+      // this tile's registers are consumed: the next tile's loads go out now (none after the
+      // last tile, so that nothing is left in flight when the results are written)
+      if (k + 1 < n) issue(k + 1);
 
       // online softmax: lane holds tokens 4*grp + e of head r16
       float sv[4], mx = kNegBig;
