@@ -114,7 +114,7 @@ def _cpu_model() -> str:
 def cpu_baseline(w, budget_s=15.0):
     """The fp64 oracle on the host cores over a bounded sample of the same workload: the first
     sequences, as many as one pass of about budget_s / 3 seconds covers, timed three times
-    (median reported), then once more on one thread over the same sample."""
+    (median reported), then three times more on one thread over the same sample."""
     import numpy as np
     import torch
 
@@ -163,13 +163,19 @@ def cpu_baseline(w, budget_s=15.0):
     n_threads = torch.get_num_threads()
     try:
         torch.set_num_threads(1)
-        if threadpool_limits is not None:
-            with threadpool_limits(limits=1):
-                b1, t1 = one_pass(small)
-        else:
-            b1, t1 = one_pass(small)
+        passes = []
+        for _ in range(3):
+            if threadpool_limits is not None:
+                with threadpool_limits(limits=1):
+                    passes.append(one_pass(small))
+            else:
+                passes.append(one_pass(small))
+        b1 = passes[0][0]
+        t1 = float(np.median([t for _, t in passes]))
         single = {"value": round(b1 / t1 / 1e9, 4), "unit": "GB/s", "cores": 1,
-                  "sample": f"the same {len(small)} sequences ({b1 / 1e6:.1f} MB of K/V, {t1:.1f} s)"}
+                  "runs": [round(b / t / 1e9, 4) for b, t in passes],
+                  "sample": f"the same {len(small)} sequences ({b1 / 1e6:.1f} MB of K/V, median of 3 passes "
+                            f"of {t1:.1f} s)"}
     finally:
         torch.set_num_threads(n_threads)
     all_cores = {"value": round(float(np.median(runs)), 4), "unit": "GB/s", "cores": cores,
@@ -182,7 +188,7 @@ def cpu_baseline(w, budget_s=15.0):
             "kind": "oracle",
             "sample": f"first {len(sample)} of {sp.num_seqs} sequences of the same workload "
                       f"({nbytes / 1e6:.1f} MB of K/V per pass), fp64 numpy, upcast inside the timer; "
-                      f"all cores: median of 3 timed passes after a warm-up; one thread: one pass; the "
+                      f"all cores: median of 3 timed passes after a warm-up; one thread: median of 3 passes; the "
                       f"faster is reported; host cores available {len(os.sched_getaffinity(0))}",
             "all_cores": all_cores,
             "single_thread": single,
@@ -578,7 +584,11 @@ def main():
         "roofline": {
             "kernel": ("pkv_paged_attn_decode_prefix" if args.prefix_shared else
                        "pkv_paged_attn_decode" if args.separate else "pkv_paged_attn_decode_append") +
-                      " (decode kernel + merge of sequences cut by the split)",
+                      (" (prefix kernel, decode over the suffixes, merge of sequences cut by the split, "
+                       "combine)" if args.prefix_shared else
+                       f" (fixed partitions of {part} tokens: decode kernel, then a reduce when a "
+                       f"sequence spans several)" if part else
+                       " (decode kernel + merge of sequences cut by the split)"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

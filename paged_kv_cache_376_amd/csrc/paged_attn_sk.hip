@@ -266,8 +266,8 @@ void decode_sk_kernel(SkParams p) {
     // id is outside the pool).  A tile that opens a sequence also brings that sequence's
     // query; with a fused append, the last tile of a sequence also brings its new K/V row.
     // The buffer resource starts at the tile's first row: rows r16 are read at r16 * tok_bytes.
-    // With 8-token blocks rows 8-15 come from a second block, through a second resource whose
-    // base sits 8 rows before that block.
+    // With 8-token blocks rows 8-15 come from a second block (nrec1: the bytes of rows 0-15
+    // counted from 8 rows before that block).
     auto issue = [&](int kk) {
       int phys = 0, nrec = 0, phys1 = 0, nrec1 = 0, half = 0;
       if (kk < n) {
@@ -303,22 +303,28 @@ void decode_sk_kernel(SkParams p) {
           phys1 = nrec1 ? phys1 : 0;
         }
       }
-      const int64_t off = phys * block_bytes + half * kTile * tok_bytes;
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(kbase + off, 0, nrec, kRsrcWord3);
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(vbase + off, 0, nrec, kRsrcWord3);
-      if (BS != 8 || r16 < 8) {
+      if constexpr (BS == 8) {
+        // Rows 0-7 come from block phys and rows 8-15 from block phys1, so the two halves of
+        // the wave would need different buffer resources.  Per-lane 64-bit addresses (global
+        // loads) avoid that; a lane whose row is past the rows in use, or whose block id lies
+        // outside the pool, loads nothing and keeps zeros.
+        const bool lo = r16 < 8;
+        const bool ok = r16 * tok_bytes < (lo ? nrec : nrec1);
+        const int64_t a = (lo ? phys : phys1) * block_bytes + (r16 & 7) * tok_bytes + g * ROW + grp * 16;
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          kbuf[c] = ok ? *reinterpret_cast<const u32x4*>(kbase + a + c * 64) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          vbuf[c] = ok ? *reinterpret_cast<const u32x4*>(vbase + a + c * 64) : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        const int64_t off = phys * block_bytes + half * kTile * tok_bytes;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(kbase + off, 0, nrec, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(vbase + off, 0, nrec, kRsrcWord3);
 #pragma unroll
         for (int c = 0; c < KC; ++c) kbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff + c * 64, 0, 0);
 #pragma unroll
         for (int c = 0; c < KC; ++c) vbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + c * 64, 0, 0);
-      } else {
-        const int64_t off1 = phys1 * block_bytes - 8 * tok_bytes;
-        const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc(kbase + off1, 0, nrec1, kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t rv1 = __builtin_amdgcn_make_buffer_rsrc(vbase + off1, 0, nrec1, kRsrcWord3);
-#pragma unroll
-        for (int c = 0; c < KC; ++c) kbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rk1, voff + c * 64, 0, 0);
-#pragma unroll
-        for (int c = 0; c < KC; ++c) vbuf[c] = __builtin_amdgcn_raw_buffer_load_b128(rv1, voff + c * 64, 0, 0);
       }
     };
     issue(0);
