@@ -94,23 +94,27 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void prefix_kernel(PrefixParams 
         phys1 = nrec1 ? phys1 : 0;
       }
     }
-    const int64_t off = phys * block_bytes + hf * kTile * tok_bytes;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kbase) + off, 0, nrec, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(vbase) + off, 0, nrec, kRsrcWord3);
-    if (BS != 8 || r16 < 8) {
+    if constexpr (BS == 8) {
+      // rows 8-15 of the tile are rows 0-7 of the second 8-token block: per-lane 64-bit
+      // addresses rather than a buffer resource that differs between the two halves of the wave
+      // (a lane whose block id lies outside the pool loads nothing and keeps zeros)
+      const bool lo = r16 < 8;
+      const bool ok = r16 * tok_bytes < (lo ? nrec : nrec1);
+      const int64_t a = (lo ? phys : phys1) * block_bytes + (r16 & 7) * tok_bytes + g * ROW + grp * 16;
+#pragma unroll
+      for (int cc = 0; cc < KC; ++cc)
+        kbuf[cc] = ok ? *reinterpret_cast<const u32x4*>(kbase + a + cc * 64) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int cc = 0; cc < KC; ++cc)
+        vbuf[cc] = ok ? *reinterpret_cast<const u32x4*>(vbase + a + cc * 64) : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      const int64_t off = phys * block_bytes + hf * kTile * tok_bytes;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kbase) + off, 0, nrec, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(vbase) + off, 0, nrec, kRsrcWord3);
 #pragma unroll
       for (int cc = 0; cc < KC; ++cc) kbuf[cc] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff + cc * 64, 0, 0);
 #pragma unroll
       for (int cc = 0; cc < KC; ++cc) vbuf[cc] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + cc * 64, 0, 0);
-    } else {
-      // rows 8-15 of the tile are rows 0-7 of the second 8-token block
-      const int64_t off1 = phys1 * block_bytes - 8 * tok_bytes;
-      const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kbase) + off1, 0, nrec1, kRsrcWord3);
-      const __amdgpu_buffer_rsrc_t rv1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(vbase) + off1, 0, nrec1, kRsrcWord3);
-#pragma unroll
-      for (int cc = 0; cc < KC; ++cc) kbuf[cc] = __builtin_amdgcn_raw_buffer_load_b128(rk1, voff + cc * 64, 0, 0);
-#pragma unroll
-      for (int cc = 0; cc < KC; ++cc) vbuf[cc] = __builtin_amdgcn_raw_buffer_load_b128(rv1, voff + cc * 64, 0, 0);
     }
   };
   // Writes this wave's loaded tile into LDS buffer b, tile slot `wave`.
