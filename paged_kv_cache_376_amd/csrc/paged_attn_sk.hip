@@ -591,7 +591,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
   constexpr int U = 4;  // records in flight per wave after the first pair
   const int hgroups = (p.num_kv_heads + kHeads - 1) / kHeads;
   const int r = blockIdx.x / hgroups, hg = blockIdx.x % hgroups;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r16 = lane & 15,
+            grp = lane >> 4;
   const int hw = wave % kHeads, pw = wave / kHeads;
   const int g = hg * kHeads + hw;
   const bool live = g < p.num_kv_heads;
@@ -620,7 +621,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
   float2* s_ml = reinterpret_cast<float2*>(s_merge + hw * (NC * 64 * 16 + 64 * 8) + NC * 64 * 16);
   __shared__ int s_ready[kHeads];  // wave row 1 has left its partial result for head column hw
 
-  const int4 d = *reinterpret_cast<const int4*>(p.ws_desc + 4 * r);
+  const int4 dl = *reinterpret_cast<const int4*>(p.ws_desc + 4 * r);
+  // the descriptor is the same for every lane: keep it in scalar registers, so that the record
+  // loads below take wave-uniform buffer resources
+  const int4 d = make_int4(__builtin_amdgcn_readfirstlane(dl.x), __builtin_amdgcn_readfirstlane(dl.y),
+                           __builtin_amdgcn_readfirstlane(dl.z), 0);
   float2 ml0[2];
   f32x4 x0[2][NC];
   const bool first = pw == 0 && live && r > 0;
