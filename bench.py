@@ -564,6 +564,8 @@ def main():
         "decode_tokens_per_s_per_layer": round(sp.num_seqs / (ms_step / 1e3), 1),
         "decode_tokens_per_s_70b_shape_attention_only": round(sp.num_seqs / (LAYERS_70B * ms_step / 1e3), 1),
         "append_us": None if t_app is None else round(float(t_app.mean()) * 1e3, 2),
+        # the append's algorithmic bytes (new rows read and written, 8-byte slots) over its time
+        "append_gbs": None if t_app is None else round((app_bytes + 8 * sp.num_seqs) / (float(t_app.mean()) / 1e3) / 1e9, 2),
         "decode_us_median": round(float(np.median(t_dec)) * 1e3, 2),
         "decode_us_p10": round(float(np.percentile(t_dec, 10)) * 1e3, 2),
         "decode_us_p90": round(float(np.percentile(t_dec, 90)) * 1e3, 2),

@@ -35,7 +35,9 @@
 //                            ds_read_b64_tr_b16 (one transposing read per 16-column chunk)
 // Loads use buffer resources that end at the tile's last row in use: the rows of a partly
 // filled last tile past the context, and a tile whose block id lies outside the pool, read as
-// zeros with no memory access, so the loads need no branches around them.
+// zeros with no memory access, so the loads need no branches around them.  (With 8-token
+// blocks a tile spans two blocks; there each lane loads through its own 64-bit address,
+// masked the same way.)
 #include <hip/hip_runtime.h>
 
 #include <cmath>
