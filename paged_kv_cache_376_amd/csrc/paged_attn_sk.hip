@@ -645,13 +645,53 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
 #pragma unroll
     for (int q = 0; q < NC; ++q) a[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (first) fold_records<2, NC>(m, l, a, ml0, x0, 2);
-    for (int c0 = r + 1 + U * pw; live && c0 <= rb; c0 += 2 * U) {
-      float2 ml[U];
-      f32x4 x[U][NC];
+    if (G <= 8) {
+      // Two records per load: a record holds G <= 8 rows, so lanes r16 < 8 take ranges
+      // c0 .. c0+3 and lanes r16 >= 8 ranges c0+4 .. c0+7, each lane the row r16 & 7 of its
+      // record, and one round of four loads folds eight ranges (a sequence spanning up to 17
+      // ranges needs one round per wave row).  The two halves fold apart (the second starts
+      // empty) and are combined at the end, first half first: a fixed order.
+      const int half = r16 >> 3, row = r16 & 7, hr8 = row < G ? row : 0;
+      if (half) {
+        m = kNegBig;
+        l = 0.f;
 #pragma unroll
-      for (int u = 0; u < U; ++u) load_rec_if(rec_of(c0 + u <= rb ? c0 + u : c0, 0), c0 + u <= rb, ml[u], x[u]);
-      __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the first use
-      fold_records<U, NC>(m, l, a, ml, x, rb - c0 + 1);
+        for (int q = 0; q < NC; ++q) a[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      for (int c0 = r + 1 + 2 * U * pw; live && c0 <= rb; c0 += 4 * U) {
+        const int cb = c0 + U * half;  // this half's first range
+        float2 ml[U];
+        f32x4 x[U][NC];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const bool ok = cb + u <= rb;  // a record past rb is not loaded
+          const int64_t rec = rec_of(ok ? cb + u : r, 0);
+          ml[u] = ok ? *reinterpret_cast<const float2*>(p.ws_ml + rec * 32 + hr8 * 2) : make_float2(kNegBig, 0.f);
+#pragma unroll
+          for (int q = 0; q < NC; ++q)
+            x[u][q] = ok ? *reinterpret_cast<const f32x4*>(p.ws_acc + rec * (16 * D) + hr8 * D + 16 * q + 4 * grp)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the first use
+        fold_records<U, NC>(m, l, a, ml, x, min(U, max(0, rb - cb + 1)));
+      }
+      // the second half's result (same row, lane ^ 8) folded into the first half's
+      float2 mlo[1] = {make_float2(__shfl_xor(m, 8, 64), __shfl_xor(l, 8, 64))};
+      f32x4 xo[1][NC];
+#pragma unroll
+      for (int q = 0; q < NC; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xo[0][q][e] = __shfl_xor(a[q][e], 8, 64);
+      if (!half) fold_records<1, NC>(m, l, a, mlo, xo, 1);
+    } else {
+      for (int c0 = r + 1 + U * pw; live && c0 <= rb; c0 += 2 * U) {
+        float2 ml[U];
+        f32x4 x[U][NC];
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_rec_if(rec_of(c0 + u <= rb ? c0 + u : c0, 0), c0 + u <= rb, ml[u], x[u]);
+        __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the first use
+        fold_records<U, NC>(m, l, a, ml, x, rb - c0 + 1);
+      }
     }
     if (pw == 1) {  // hand the partial result to wave row 0 (no work-group barrier: row 1 goes on)
 #pragma unroll
