@@ -555,8 +555,10 @@ void decode_sk_kernel(SkParams p) {
 // first tile in range r - 1 and spans ranges r - 1 .. rb, so its first two records (range
 // r - 1, slot 1; range r, slot 0) are loaded before the descriptor arrives.  Two waves serve
 // each KV head of the group: after that first pair (wave row 0), the records of ranges
-// r + 1 + 4k .. r + 4 + 4k go to wave row k % 2, four loads in flight; wave row 0 then adds row
-// 1's result and writes the output.  The order is fixed: deterministic.
+// r + 1 + 4k .. r + 4 + 4k go to wave row k % 2, four loads in flight (with at most 8 query
+// heads per KV head a load carries two records, one per half of the wave, so a row takes
+// eight ranges per round); wave row 0 then adds row 1's result and writes the output.  The
+// order is fixed: deterministic.
 //
 // With a fused append the decode kernel took each sequence's new K/V row from new_key /
 // new_value; wave row 1 of this kernel writes those rows to their pool slots (position
