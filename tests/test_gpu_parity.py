@@ -190,3 +190,19 @@ def test_batch_at_the_even_split_limit(fused):
             b, o = int(slots[s]) // bs, int(slots[s]) % bs
             assert torch.equal(cache.k_cache[b, o].cpu().view(torch.int16), w.new_k[s].view(torch.int16))
             assert torch.equal(cache.v_cache[b, o].cpu().view(torch.int16), w.new_v[s].view(torch.int16))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("g", [1, 3, 5, 8, 9, 12, 16])
+def test_group_sizes_with_long_merge_chains(g, d):
+    """Every group size class of the even split: G <= 8 (the merge folds two records per load,
+    one per half-wave) and G > 8 (one record per load), odd G, at D 64 and 128.  Long contexts
+    among short and empty ones: with few sequences the ranges are short, so a 4000-token
+    sequence is cut into some thirty ranges and its records are folded over several rounds."""
+    lens = (4000, 33, 2500, 0, 700)
+    say(f"[parity groups] G={g} D={d}")
+    w = W.Workload(W.Spec("groups", "bfloat16", len(lens), 2 * g, 2, d, "fixed", fixed_lengths=lens), seed=40 + g)
+    out, *_ = decode_step(w, partition_size=0)
+    err = max_err(out, oracle_out(w))
+    say(f"    max abs err {err:.3e}")
+    assert torch.isfinite(out.float()).all() and err <= TOL["bfloat16"]
