@@ -51,11 +51,11 @@ namespace pkv {
 namespace sk {
 namespace {
 
-// Work-group shape: kHeads KV heads side by side (their waves read neighbouring slices of the
-// same token rows together) x kSplits consecutive sub-ranges of the tile list (merged in LDS).
-constexpr int kHeads = 4;
-constexpr int kSplits = 2;
-constexpr int kWaves = kHeads * kSplits;
+// Work-group shape: 8 waves, HEADS KV heads side by side (their waves read neighbouring slices
+// of the same token rows together) x 8 / HEADS consecutive sub-ranges of the tile list (merged
+// in LDS).  HEADS is 4, or 1 for small batches: there a sequence is cut into many ranges, and
+// eight sub-ranges merged in LDS leave a quarter of the records to the merge kernel.
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kLast = 1 << 8;             // tile flag: last tile of its sequence
 constexpr int kFirst = 1 << 9;            // tile flag: first tile of its sequence
@@ -153,9 +153,10 @@ __host__ __device__ inline int sk_lds_bytes(int B, int D, int G) {
 
 // SUFFIX: suffix and partial-result mode (seq_start and part_out set), compiled apart so that
 // the plain decode carries none of it.
-template <typename T, int D, int BS, bool SUFFIX>
+template <typename T, int D, int BS, bool SUFFIX, int HEADS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_sk_kernel(SkParams p) {
+  constexpr int kHeads = HEADS, kSplits = kWaves / HEADS;
   using M = Mma<T>;
   using raw = typename T::raw;
   constexpr int ROW = D * 2;                   // bytes of one head row
@@ -566,7 +567,10 @@ void decode_sk_kernel(SkParams p) {
 // r + ranges, ...  Wave row 0 waits for row 1's partial result on an LDS flag rather than a
 // work-group barrier, so the append does not hold up the merge.
 constexpr int kMergeThreads = 512;
-__host__ __device__ inline int merge_lds_bytes(int D) { return kHeads * ((D / 16) * 64 * 16 + 64 * 8); }
+// LDS of the merge kernel: for each head column, the partial results of wave rows 1 .. rows-1.
+__host__ __device__ inline int merge_lds_bytes(int D, int heads) {
+  return heads * (kWaves / heads - 1) * ((D / 16) * 64 * 16 + 64 * 8);
+}
 
 // Folds U records (loaded into x / ml; u valid when u < nvalid) into the running (m, l, a).
 template <int U, int NC>
@@ -588,8 +592,9 @@ __device__ __forceinline__ void fold_records(float& m, float& l, f32x4* a, const
   m = mn;
 }
 
-template <typename T, int D>
+template <typename T, int D, int HEADS>
 __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
+  constexpr int kHeads = HEADS, kRows = kWaves / HEADS;  // wave rows per KV head
   using raw = typename T::raw;
   constexpr int NC = D / 16;
   constexpr int U = 4;  // records in flight per wave after the first pair
@@ -621,9 +626,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
       x[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (hr * D + 16 * q + 4 * grp) * 4, 0, 0));
   };
   extern __shared__ __attribute__((aligned(16))) unsigned char s_merge[];
-  f32x4* s_a = reinterpret_cast<f32x4*>(s_merge + hw * (NC * 64 * 16 + 64 * 8));
-  float2* s_ml = reinterpret_cast<float2*>(s_merge + hw * (NC * 64 * 16 + 64 * 8) + NC * 64 * 16);
-  __shared__ int s_ready[kHeads];  // wave row 1 has left its partial result for head column hw
+  // partial result of wave row j >= 1 of head column hw
+  auto slot = [&](int j) { return s_merge + (hw * (kRows - 1) + j - 1) * (NC * 64 * 16 + 64 * 8); };
+  auto s_a = [&](int j) { return reinterpret_cast<f32x4*>(slot(j)); };
+  auto s_ml = [&](int j) { return reinterpret_cast<float2*>(slot(j) + NC * 64 * 16); };
+  __shared__ int s_ready[kWaves];  // wave row pw of head column hw has left its partial result
 
   const int4 dl = *reinterpret_cast<const int4*>(p.ws_desc + 4 * r);
   // the descriptor is the same for every lane: keep it in scalar registers, so that the record
@@ -637,7 +644,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
     load_rec(rec_of(r - 1, 1), ml0[0], x0[0]);
     load_rec(rec_of(r, 0), ml0[1], x0[1]);
   }
-  if (tid < kHeads) s_ready[tid] = 0;
+  if (tid < kWaves) s_ready[tid] = 0;
   __syncthreads();
 
   if (d.x >= 0) {  // uniform over the work-group
@@ -660,7 +667,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
 #pragma unroll
         for (int q = 0; q < NC; ++q) a[q] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      for (int c0 = r + 1 + 2 * U * pw; live && c0 <= rb; c0 += 4 * U) {
+      for (int c0 = r + 1 + 2 * U * pw; live && c0 <= rb; c0 += 2 * U * kRows) {
         const int cb = c0 + U * half;  // this half's first range
         float2 ml[U];
         f32x4 x[U][NC];
@@ -686,7 +693,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
         for (int e = 0; e < 4; ++e) xo[0][q][e] = __shfl_xor(a[q][e], 8, 64);
       if (!half) fold_records<1, NC>(m, l, a, mlo, xo, 1);
     } else {
-      for (int c0 = r + 1 + U * pw; live && c0 <= rb; c0 += 2 * U) {
+      for (int c0 = r + 1 + U * pw; live && c0 <= rb; c0 += U * kRows) {
         float2 ml[U];
         f32x4 x[U][NC];
 #pragma unroll
@@ -695,43 +702,44 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
         fold_records<U, NC>(m, l, a, ml, x, rb - c0 + 1);
       }
     }
-    if (pw == 1) {  // hand the partial result to wave row 0 (no work-group barrier: row 1 goes on)
+    if (pw >= 1) {  // hand the partial result to wave row 0 (no work-group barrier: the row goes on)
 #pragma unroll
-      for (int q = 0; q < NC; ++q) s_a[q * 64 + lane] = a[q];
-      s_ml[lane] = make_float2(m, l);
-      __hip_atomic_store(&s_ready[hw], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      for (int q = 0; q < NC; ++q) s_a(pw)[q * 64 + lane] = a[q];
+      s_ml(pw)[lane] = make_float2(m, l);
+      __hip_atomic_store(&s_ready[hw * kRows + pw], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     } else {
-      // row 1 of the same work-group always sets the flag; the cap only bounds the wait
-      for (int spin = 0; spin < (1 << 22) &&
-                         __hip_atomic_load(&s_ready[hw], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
-           ++spin)
-        __builtin_amdgcn_s_sleep(1);
+      // the other rows of the same work-group always set their flags; the cap only bounds the
+      // wait.  Their results are folded in row order: a fixed order.
+      for (int j = 1; j < kRows; ++j) {
+        for (int spin = 0; spin < (1 << 22) &&
+                           __hip_atomic_load(&s_ready[hw * kRows + j], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
+             ++spin)
+          __builtin_amdgcn_s_sleep(1);
+        float2 mlj[1] = {s_ml(j)[lane]};
+        f32x4 xj[1][NC];
+#pragma unroll
+        for (int q = 0; q < NC; ++q) xj[0][q] = s_a(j)[q * 64 + lane];
+        fold_records<1, NC>(m, l, a, mlj, xj, 1);
+      }
       if (live && r16 < G) {
-        const float2 o1 = s_ml[lane];
-        const float mn = fmaxf(m, o1.x);
-        const float f0 = __builtin_amdgcn_exp2f(m - mn), f1 = __builtin_amdgcn_exp2f(o1.x - mn);
-        const float L = l * f0 + o1.y * f1;
-        const float inv = L > 0.f ? 1.f / L : 0.f;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
         const int64_t orow = static_cast<int64_t>(s) * p.num_q_heads + g * G + r16;
         if (p.part_out) {
-          f32x4 r[NC];
-#pragma unroll
-          for (int q = 0; q < NC; ++q) r[q] = a[q] * f0 + s_a[q * 64 + lane] * f1;
-          store_partial<D>(p, orow, r, inv, mn, L, grp);
+          store_partial<D>(p, orow, a, inv, m, l, grp);
         } else {
           raw* o = static_cast<raw*>(p.out) + orow * D;
 #pragma unroll
-          for (int q = 0; q < NC; ++q) store4<T>(o + 16 * q + 4 * grp, (a[q] * f0 + s_a[q * 64 + lane] * f1) * inv);
+          for (int q = 0; q < NC; ++q) store4<T>(o + 16 * q + 4 * grp, a[q] * inv);
         }
       }
     }
   }
 
-  if (p.new_key != nullptr && pw == 1) {  // fused append (wave row 1): new rows to their slots
+  if (p.new_key != nullptr && pw >= 1) {  // fused append (wave rows 1 ..): new rows to their slots
     constexpr int CPR = D * static_cast<int>(sizeof(raw)) / 16;  // 16-byte chunks per row
-    constexpr int kRowThreads = kMergeThreads / 2;
+    constexpr int kRowThreads = 64 * kHeads * (kRows - 1);
     const int64_t row_bytes = static_cast<int64_t>(D) * sizeof(raw);
-    const int t = tid - kRowThreads, ch = 16 * (t % CPR);
+    const int t = tid - 64 * kHeads, ch = 16 * (t % CPR);
     const int nseq = (p.num_seqs - r + p.ranges - 1) / p.ranges;
     for (int pi = t / CPR; pi < nseq * kHeads; pi += kRowThreads / CPR) {
       const int s = r + p.ranges * (pi / kHeads), gg = hg * kHeads + pi % kHeads;
@@ -751,26 +759,31 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
   }
 }
 
-template <typename T, int D, int BS>
+template <typename T, int D, int BS, int HEADS>
 hipError_t launch(const SkParams& p, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(sk_lds_bytes(p.num_seqs, D, p.group));
-  const int hgroups = (p.num_kv_heads + kHeads - 1) / kHeads;
+  const int hgroups = (p.num_kv_heads + HEADS - 1) / HEADS;
   if (p.seq_start)
-    hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, true>), dim3(p.ranges * hgroups), dim3(kThreads), lds, stream, p);
+    hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, true, HEADS>), dim3(p.ranges * hgroups), dim3(kThreads), lds, stream, p);
   else
-    hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, false>), dim3(p.ranges * hgroups), dim3(kThreads), lds, stream, p);
+    hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, false, HEADS>), dim3(p.ranges * hgroups), dim3(kThreads), lds, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((merge_sk_kernel<T, D>), dim3(p.ranges * hgroups), dim3(kMergeThreads),
-                     static_cast<size_t>(merge_lds_bytes(D)), stream, p);
+  hipLaunchKernelGGL((merge_sk_kernel<T, D, HEADS>), dim3(p.ranges * hgroups), dim3(kMergeThreads),
+                     static_cast<size_t>(merge_lds_bytes(D, HEADS)), stream, p);
   return hipGetLastError();
+}
+
+template <typename T, int D, int BS>
+hipError_t launch_heads(const SkParams& p, hipStream_t stream) {
+  return sk_heads(p.num_seqs) == 1 ? launch<T, D, BS, 1>(p, stream) : launch<T, D, BS, 4>(p, stream);
 }
 
 template <typename T, int D>
 hipError_t launch_bs(const SkParams& p, hipStream_t stream) {
-  if (p.block_size == 8) return launch<T, D, 8>(p, stream);
-  if (p.block_size == 32) return launch<T, D, 32>(p, stream);
-  return launch<T, D, 16>(p, stream);
+  if (p.block_size == 8) return launch_heads<T, D, 8>(p, stream);
+  if (p.block_size == 32) return launch_heads<T, D, 32>(p, stream);
+  return launch_heads<T, D, 16>(p, stream);
 }
 
 }  // namespace
@@ -782,7 +795,8 @@ int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_le
   // 32 tiles per range) without ranges so short that merging their records dominates.
   const int64_t max_blocks = (static_cast<int64_t>(max_context_len) + kTile - 1) / kTile;
   const int64_t upper_tiles = static_cast<int64_t>(num_seqs) * max_blocks;
-  const int64_t hgroups = (num_kv_heads + kHeads - 1) / kHeads;
+  const int64_t heads = sk_heads(num_seqs);
+  const int64_t hgroups = (num_kv_heads + heads - 1) / heads;
   int64_t r = kSkTargetWaves / (hgroups * kWaves);
   if (r < 1) r = 1;
   const int64_t cap = (upper_tiles + 7) / 8;

@@ -48,6 +48,10 @@ struct SkParams {
   float* part_lse;
 };
 
+// KV heads per work-group of the even split for a batch of num_seqs sequences: 4, or 1 below
+// 8 sequences.  A small batch is cut into many ranges per sequence; one head per work-group
+// with eight sub-ranges merged in LDS leaves the merge kernel a quarter of the records.
+inline int32_t sk_heads(int32_t num_seqs) { return num_seqs < 8 ? 1 : 4; }
 // Ranges per KV head for these arguments (host).
 int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len);
 // LDS bytes of the decode kernel for these shapes (host); above 64 KiB needs no opt-in here.
