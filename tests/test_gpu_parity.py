@@ -206,3 +206,23 @@ def test_group_sizes_with_long_merge_chains(g, d):
     err = max_err(out, oracle_out(w))
     say(f"    max abs err {err:.3e}")
     assert torch.isfinite(out.float()).all() and err <= TOL["bfloat16"]
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("n", [1, 3, 7])
+def test_small_batch_fused_append(n, bs):
+    """Batches under 8 sequences (one KV head per work-group, eight sub-ranges merged in LDS):
+    the fused call's output against the oracle and the appended rows in their slots bit for
+    bit, with contexts long enough to be cut into many ranges, at each block size."""
+    lens = tuple(int(x) for x in np.random.default_rng(50 + n).integers(1, 6000, size=n))
+    say(f"[parity small batch] n={n} block={bs} lens={lens}")
+    w = W.Workload(W.Spec("small", "bfloat16", n, 64, 8, 128, "fixed", fixed_lengths=lens, block_size=bs),
+                   seed=51 + n)
+    out, cache, _, _, _, slots = decode_step_fused(w)
+    err = max_err(out, oracle_out(w))
+    say(f"    max abs err {err:.3e}")
+    assert err <= TOL["bfloat16"]
+    for s in range(n):
+        b, o = int(slots[s]) // bs, int(slots[s]) % bs
+        assert torch.equal(cache.k_cache[b, o].cpu().view(torch.int16), w.new_k[s].view(torch.int16))
+        assert torch.equal(cache.v_cache[b, o].cpu().view(torch.int16), w.new_v[s].view(torch.int16))

@@ -54,6 +54,10 @@ CASES = [
                    suffix_lo=0, suffix_hi=90)),
     ("bs8", W.SPECS["prefix_bf16"].replace(num_seqs=16, prefix_len=200, suffix_hi=100, block_size=8)),
     ("bs32", W.SPECS["prefix_bf16"].replace(num_seqs=16, prefix_len=200, suffix_hi=100, block_size=32)),
+    # a batch under 8 sequences (one KV head per decode work-group) with suffixes long enough
+    # to be cut into many ranges
+    ("small-batch", W.SPECS["prefix_bf16"].replace(num_seqs=6, group_size=3, prefix_len=300, suffix_lo=1000,
+                                                   suffix_hi=3000)),
 ]
 
 
