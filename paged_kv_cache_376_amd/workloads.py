@@ -24,6 +24,8 @@ for this path, so these stand in for the serving traffic they describe):
 * ``prefix_bf16``   -- 16 groups of 8 sequences; each group shares one 1024-token prefix
   (the pages' input length 1024), then every sequence has a private suffix of 1..512
   tokens; 64 query / 8 KV heads, D 128, bf16.
+* ``single_long_bf16`` -- one sequence of 32768 tokens, 64 query / 8 KV heads, D 128, bf16
+  (batch-1 long-context decode, beside the five above).
 
 Block size is 16 everywhere.  The pool holds 10% more blocks than the workload needs,
 counting the block each sequence may take for the appended token (``tiny_fp32`` uses 64).
@@ -81,6 +83,10 @@ SPECS = {
                       fixed_lengths=(32768,) * 8),
     "prefix_bf16": Spec("prefix_bf16", "bfloat16", 128, 64, 8, 128, "prefix",
                         prefix_len=1024, group_size=8, suffix_lo=1, suffix_hi=512),
+    # one long sequence at the 70B head shape (batch-1 long-context decode; not one of the
+    # five workloads above)
+    "single_long_bf16": Spec("single_long_bf16", "bfloat16", 1, 64, 8, 128, "fixed",
+                             fixed_lengths=(32767,)),
 }
 
 # Stream indices under SeedSequence(seed).spawn(_NUM_STREAMS)
