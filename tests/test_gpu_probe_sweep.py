@@ -30,8 +30,10 @@ CASES = [
     ("one-32768-gqa-bf16", "bfloat16", 64, 8, 128, (32768,), 16, 0),
     ("one-9000-fp16-bs8", "float16", 16, 2, 64, (9000,), 8, 0),
     ("three-bf16-bs32", "bfloat16", 32, 4, 128, (6000, 37, 2049), 32, 0),
+    ("two-mha-fp16", "float16", 32, 32, 128, (5000, 1234), 16, 0),              # group size 1
     # eight sequences or more: four KV heads per work-group, 2 sub-ranges each
     ("eight-bf16", "bfloat16", 16, 2, 128, (4096, 4096, 1, 4096, 700, 3, 4096, 2500), 16, 0),
+    ("nine-mha-bf16", "bfloat16", 8, 8, 64, (1500, 1, 999, 1500, 16, 17, 1500, 640, 1100), 16, 0),
     ("ten-fp16-fixed-256", "float16", 24, 3, 64, (3000, 17, 256, 257, 1500, 2, 999, 3000, 64, 1000), 16, 256),
 ]
 
