@@ -115,10 +115,20 @@ PKV_API pkv_status pkv_kv_cache_append(const void* key, const void* value,
 
 /* Bytes of workspace pkv_paged_attn_decode needs for these arguments (0 when the chosen
  * work split needs none), partition_size and dtype (a pkv_dtype) as for the decode call.
- *   - partition_size 0 with f16/bf16 pools and at most 8192 sequences: the even split over the
- *     GPU; the workspace holds, per work range, fp32 records of sequences cut by the split (two
- *     per KV head, 16*head_dim + 32 floats each) and one 16-byte descriptor; it does not
- *     depend on the context lengths beyond max_context_len nor on the block size.
+ *   - partition_size 0 with f16/bf16 pools and at most 8192 sequences whose decode state fits
+ *     one work-group's 160 KiB of LDS (about 8 bytes per sequence plus
+ *     16 * group * head_dim * 4 bytes of wave states: every batch up to 8192 for groups up to
+ *     8 at head_dim 128, up to 3807 sequences at group 16): the even split over the GPU.  The
+ *     workspace holds a status word (the first 256 bytes are reserved for it, see below), then,
+ *     per work range, fp32 records of sequences cut by the split (two per KV head,
+ *     16*head_dim + 32 floats each) and one 16-byte descriptor; it does not depend on the
+ *     context lengths beyond max_context_len nor on the block size.
+ *     Status word: the first int32 of the workspace.  The decode launch clears it and the
+ *     merge launch sets it to 1 if one of its bounded waits (a wave waiting on an LDS flag of
+ *     another wave of its own work-group) ran out of polls; the call's output is then not
+ *     reliable.  Read it once the stream has finished the call; 0 means every wait ended
+ *     normally.  (Co-resident waves of one work-group always set their flags, so the limit
+ *     only bounds the wait; pkv_set_merge_spin_limit lowers it to test this path.)
  *   - otherwise (f32 pools, or an explicit partition_size): fixed partitions; fp32 partials of
  *     split sequences, num_seqs * num_q_heads * P * (head_dim + 2) floats with P partitions
  *     of the longest context, 0 when nothing is split.
@@ -227,8 +237,9 @@ PKV_API pkv_status pkv_paged_attn_decode_append(void* out, const void* q,
  * Sequences that share the physical blocks of the start of their contexts (prefix sharing by
  * reference to the same blocks, [yunthe] section "PagedAttention分页注意力机制原理"; one block
  * shared by several requests, [111cn] §3.2) attend over that shared prefix in one pass for
- * the whole group: a work-group takes 16 prefix tiles of one KV head and its waves take the
- * group's query rows (member x query head), so every prefix tile is read once for the group.
+ * the whole group: a work-group takes 32 prefix tiles (512 tokens) of one KV head and its
+ * waves take the group's query rows (member x query head), so every prefix tile is read once
+ * for the group.
  * Each sequence's own remainder is attended by the even split over the GPU, and the two parts
  * are merged exactly with the log-sum-exp rule (fixed order: deterministic).
  *
@@ -251,9 +262,12 @@ PKV_API pkv_status pkv_paged_attn_decode_append(void* out, const void* q,
  * num_seqs and member positions outside [0, num_seqs) are skipped, prefix lengths are kept
  * inside [0, context length] on a 16-token boundary, and no more than
  * ceil(max_prefix_tokens / 512) prefix partials are read per row.
- * Errors: as pkv_paged_attn_decode; UNSUPPORTED for f32 pools or more than 8192 sequences;
- * INVALID_ARGUMENT for a bad group description (null pointers, num_groups < 0, bad
- * max_prefix_tokens). */
+ * The workspace starts with the even split's status word (see
+ * pkv_paged_attn_workspace_bytes).
+ * Errors: as pkv_paged_attn_decode; UNSUPPORTED for f32 pools, more than 8192 sequences, or a
+ * batch and group size whose decode state does not fit the LDS (see
+ * pkv_paged_attn_workspace_bytes); INVALID_ARGUMENT for a bad group description (null
+ * pointers, num_groups < 0, bad max_prefix_tokens). */
 PKV_API pkv_status pkv_paged_attn_decode_prefix(void* out, const void* q,
                                         const void* k_cache, const void* v_cache,
                                         const pkv_cache_desc* cache,
@@ -264,6 +278,14 @@ PKV_API pkv_status pkv_paged_attn_decode_prefix(void* out, const void* q,
                                         const int32_t* group_members, int32_t num_groups,
                                         int32_t max_prefix_tokens, void* workspace,
                                         size_t workspace_bytes, void* stream);
+
+/* Test hook for the merge launch's bounded waits (see the status word under
+ * pkv_paged_attn_workspace_bytes): sets the number of polls after which such a wait gives up,
+ * for every later call in this process, and returns the previous value.  A negative limit
+ * restores the default (2^22 polls).  With 0 every wait gives up at once: the call still ends
+ * normally, its output is not reliable and the status word reads 1.  Not thread-safe with
+ * respect to calls in flight on other threads. */
+PKV_API int32_t pkv_set_merge_spin_limit(int32_t limit);
 
 /* Bytes of workspace pkv_paged_attn_decode_prefix needs (the even split's, plus fp32
  * suffix results [num_seqs][num_q_heads][head_dim + 1] and prefix partials
@@ -348,15 +370,22 @@ PKV_API pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size,
                            const int32_t* free_order, pkv_block_pool** out);
 PKV_API void pkv_pool_destroy(pkv_block_pool* pool);
 
+/* Pool queries.  Each returns -1 for a NULL pool.
+ * Physical blocks in the preallocated pool ([111cn] §3.2: the cache is cut into fixed-size
+ * blocks of one physical pool). */
 PKV_API int32_t pkv_pool_num_blocks(const pkv_block_pool* pool);
+/* Tokens per block ([111cn] §3.2 and [yunthe] "PagedAttention分页注意力机制原理": 16 by default). */
 PKV_API int32_t pkv_pool_block_size(const pkv_block_pool* pool);
+/* Entries of the free list ([111cn] §3.3 free_blocks): the admission check of [111cn] §2.2
+ * compares a request's block count with this. */
 PKV_API int32_t pkv_pool_num_free(const pkv_block_pool* pool);
-/* Reference count of a block, -1 if block_id is out of range. */
+/* Reference count of a block ([gtnt] §2.1 Block.ref_count: the number of sequences whose
+ * tables name it), -1 if block_id is out of range. */
 PKV_API int32_t pkv_pool_ref_count(const pkv_block_pool* pool, int32_t block_id);
 /* Copies min(capacity, num_free) free-list entries (bottom first; the next pop takes the
- * last one) into out; returns num_free. */
+ * last one, [111cn] §3.3 pop()) into out; returns num_free. */
 PKV_API int32_t pkv_pool_free_list(const pkv_block_pool* pool, int32_t* out, int32_t capacity);
-/* Number of live sequences. */
+/* Number of live sequences: sequences holding a block table ([111cn] §3.3 block_tables). */
 PKV_API int32_t pkv_pool_num_seqs(const pkv_block_pool* pool);
 
 /* New sequence holding num_tokens (>= 0) tokens: ceil(num_tokens/bs) blocks popped from
@@ -430,7 +459,10 @@ PKV_API pkv_status pkv_pool_move_seqs(pkv_block_pool* src, pkv_block_pool* dst, 
                               int32_t* num_pairs_out);
 
 /* Block tables of seqs[0..n) as rows of tables_out[n][max_blocks_per_seq] (padded with
- * -1) and their context lengths in context_lens_out[n] (both host, nullable each).
+ * -1) and their context lengths in context_lens_out[n] (both host, nullable each): the
+ * per-sequence map from logical to physical blocks that keeps the logical token order
+ * ([111cn] §3.2), in the int32 [num_seqs][max_blocks_per_seq] form the decode kernels take
+ * (the block_tables argument of the kernel in [gtnt] §6.2).
  * NOT_FOUND, INVALID_ARGUMENT (a table longer than max_blocks_per_seq). */
 PKV_API pkv_status pkv_pool_block_tables(const pkv_block_pool* pool, const int64_t* seqs, int32_t n,
                                  int32_t max_blocks_per_seq, int32_t* tables_out,

@@ -49,6 +49,7 @@ SIGNATURES = {
     "pkv_paged_attn_decode_prefix": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, ctypes.c_float,
                                             _P, _P, _P, _I32, _I32, _P, ctypes.c_size_t, _P]),
     "pkv_paged_attn_decode_prefix_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "pkv_set_merge_spin_limit": (_I32, [_I32]),
     "pkv_pool_create": (_I32, [_I32, _I32, _PI32, ctypes.POINTER(_P)]),
     "pkv_pool_destroy": (None, [_P]),
     "pkv_pool_num_blocks": (_I32, [_P]),
@@ -273,6 +274,20 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len),
         B, Hq, float(scale), _ptr(workspace), ws_bytes, int(partition_size), _stream(stream)))
+
+
+def set_merge_spin_limit(limit: int) -> int:
+    """pkv_set_merge_spin_limit (a test hook): polls after which the merge launch's bounded
+    waits give up; a negative value restores the default.  Returns the previous limit."""
+    return int(lib().pkv_set_merge_spin_limit(int(limit)))
+
+
+def workspace_status(workspace) -> int:
+    """The status word at the start of an even-split workspace (a device tensor), read after
+    the stream has finished the call: 0, or 1 if a bounded wait of the merge launch gave up."""
+    import torch
+
+    return int(workspace.reshape(-1).view(torch.uint8)[:4].view(torch.int32).cpu().item())
 
 
 def paged_attn_decode_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,

@@ -36,6 +36,7 @@
 // including NaN, and block-table entries past ceil(ctx/16) are never read.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <type_traits>
 
@@ -552,13 +553,16 @@ hipError_t launch_dtype(const Params& p, int D, int G, hipStream_t stream) {
 using namespace pkv;
 
 namespace {
+// Poll count of the merge kernel's bounded LDS waits (pkv_set_merge_spin_limit).
+std::atomic<int32_t> g_merge_spin_limit{sk::kDefaultSpinLimit};
 // The evenly split path (16-bit pools: its products run on the bf16/f16 matrix cores) serves
-// partition_size 0 up to kSkMaxSeqs sequences; f32 pools and explicit partition sizes take
-// the fixed partitions.
-bool use_stream_k(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t partition_size,
-                  int32_t dtype) {
+// partition_size 0 up to kSkMaxSeqs sequences, as long as its prefix sum and wave states fit
+// one work-group's LDS (large groups at large batches do not); f32 pools, explicit partition
+// sizes and the shapes that do not fit take the fixed partitions.
+bool use_stream_k(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t partition_size, int32_t dtype) {
   return partition_size == 0 && (dtype == PKV_F16 || dtype == PKV_BF16) && num_kv_heads > 0 &&
-         num_q_heads % num_kv_heads == 0 && num_seqs <= sk::kSkMaxSeqs;
+         num_q_heads % num_kv_heads == 0 && sk::sk_fits(num_seqs, head_dim, num_q_heads / num_kv_heads);
 }
 }  // namespace
 
@@ -568,7 +572,7 @@ extern "C" int32_t pkv_paged_attn_partition_size(int32_t num_seqs, int32_t num_q
                                                  int32_t dtype) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
   if (max_context_len < 0 || dtype_bytes(dtype) == 0) return 0;
-  if (use_stream_k(num_seqs, num_q_heads, num_kv_heads, partition_size, dtype)) return 0;
+  if (use_stream_k(num_seqs, num_q_heads, num_kv_heads, head_dim, partition_size, dtype)) return 0;
   return resolve_partition(max_context_len, partition_size);
 }
 
@@ -578,7 +582,7 @@ extern "C" size_t pkv_paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q
                                                  int32_t dtype) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
   if (dtype_bytes(dtype) == 0) return 0;
-  if (use_stream_k(num_seqs, num_q_heads, num_kv_heads, partition_size, dtype))
+  if (use_stream_k(num_seqs, num_q_heads, num_kv_heads, head_dim, partition_size, dtype))
     return num_seqs == 0 ? 0 : sk::sk_workspace_bytes(num_seqs, num_kv_heads, head_dim, max_context_len);
   const int32_t part = resolve_partition(max_context_len, partition_size);
   if (part == 0) return 0;
@@ -637,9 +641,12 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
   const int G = num_q_heads / cache->num_kv_heads;
   if (cache->dtype == PKV_F32 ? G > 2 : G > 16)
     return fail(PKV_ERR_UNSUPPORTED, "group size %d for dtype %d (f32: <= 2, f16/bf16: <= 16)", G, cache->dtype);
-  const bool sk_path = use_stream_k(num_seqs, num_q_heads, cache->num_kv_heads, partition_size, cache->dtype);
+  const bool sk_path = use_stream_k(num_seqs, num_q_heads, cache->num_kv_heads, D, partition_size, cache->dtype);
   if (pre && !sk_path)
-    return fail(PKV_ERR_UNSUPPORTED, "prefix-shared decode needs f16/bf16 pools and at most %d sequences", sk::kSkMaxSeqs);
+    return fail(PKV_ERR_UNSUPPORTED,
+                "prefix-shared decode needs f16/bf16 pools and at most %d sequences whose decode state fits "
+                "the LDS (%d sequences, group %d, head_dim %d do not)",
+                sk::kSkMaxSeqs, num_seqs, G, D);
   if (pre && (pre->num_groups < 0 || pre->max_prefix_tokens < 0 || pre->max_prefix_tokens % 16 != 0 ||
               pre->max_prefix_tokens > max_context_len))
     return fail(PKV_ERR_INVALID_ARGUMENT, "num_groups %d, max_prefix_tokens %d (a multiple of 16, <= max_context_len)",
@@ -695,7 +702,9 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
     sp.ranges = sk::sk_ranges(num_seqs, cache->num_kv_heads, max_context_len);
     sp.scale_log2e = scale * kLog2e;
     const int64_t recs = static_cast<int64_t>(sp.ranges) * sp.num_kv_heads * 2;
-    sp.ws_acc = static_cast<float*>(workspace);
+    sp.ws_status = static_cast<int32_t*>(workspace);
+    sp.spin_limit = g_merge_spin_limit.load(std::memory_order_relaxed);
+    sp.ws_acc = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + sk::kStatusBytes);
     sp.ws_ml = sp.ws_acc + recs * 16 * D;
     sp.ws_desc = reinterpret_cast<int32_t*>(sp.ws_ml + recs * 32);
     const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -832,7 +841,7 @@ extern "C" size_t pkv_paged_attn_decode_prefix_workspace_bytes(int32_t num_seqs,
                                                                int32_t dtype) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
   if (max_prefix_tokens < 0 || max_prefix_tokens % 16 != 0 || max_prefix_tokens > max_context_len) return 0;
-  if (!use_stream_k(num_seqs, num_q_heads, num_kv_heads, 0, dtype)) return 0;
+  if (!use_stream_k(num_seqs, num_q_heads, num_kv_heads, head_dim, 0, dtype)) return 0;
   return align256(sk::sk_workspace_bytes(num_seqs, num_kv_heads, head_dim, max_context_len)) +
          prefix_extra_bytes(num_seqs, num_q_heads, head_dim, prefix_chunks(max_prefix_tokens));
 }
@@ -849,4 +858,9 @@ extern "C" pkv_status pkv_paged_attn_decode_prefix(void* out, const void* q, con
   return decode_impl(out, q, k_cache, v_cache, cache, block_tables, max_blocks_per_seq, context_lens,
                      max_context_len, num_seqs, num_q_heads, scale, workspace, workspace_bytes, 0, stream, nullptr,
                      nullptr, &pre);
+}
+
+extern "C" int32_t pkv_set_merge_spin_limit(int32_t limit) {
+  const int32_t v = limit < 0 ? sk::kDefaultSpinLimit : limit;
+  return g_merge_spin_limit.exchange(v);
 }

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void prefix_kernel(PrefixParams 
   const int ptiles = pp.seq_prefix[lead] / kTile;
   const int nk = min(ptiles - k0, kPrefixChunkTiles);
   if (nk <= 0) return;  // uniform over the work-group
-  // [2 buffers][4 tiles][K tile, V tile], rows at PITCH
+  // [2 buffers][kPrefixStep (8) tiles][K tile, V tile], rows at PITCH
   __shared__ __attribute__((aligned(16))) unsigned char s_t[2 * kPrefixStep * 2 * TILE_LDS];
 
   const int64_t tok_bytes = static_cast<int64_t>(Hkv) * ROW;

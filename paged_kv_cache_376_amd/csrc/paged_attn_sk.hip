@@ -142,7 +142,9 @@ __device__ __forceinline__ int4 tile_entry(const SkParams& p, const int* s_cu, c
 }
 
 // LDS layout of the decode kernel (dynamic): the prefix sum of block counts, then one region
-// that holds the 4 waves' V tiles during the tile loop and the 8 wave states after it.
+// that holds the 8 waves' V tiles during the tile loop and the 8 wave states after it.  The
+// kernel's static LDS (scan partials and wave flags) stays under kSkStaticLds bytes.
+constexpr int kSkStaticLds = 256;
 __host__ __device__ inline int sk_state_bytes(int D, int G) { return ((D / 16) * 4 * G * 16 + G * 8 + 15) / 16 * 16; }
 __host__ __device__ inline int sk_cu_bytes(int B) { return ((B + 1) * 4 + 15) / 16 * 16 + (B * 4 + 15) / 16 * 16; }
 __host__ __device__ inline int sk_lds_bytes(int B, int D, int G) {
@@ -185,6 +187,7 @@ void decode_sk_kernel(SkParams p) {
   unsigned char* s_work = s_dyn + sk_cu_bytes(B);              // V tiles, later wave states
   __shared__ int s_part[kWaves];
   __shared__ int s_flags[kWaves][5];
+  static_assert(sizeof(s_part) + sizeof(s_flags) <= kSkStaticLds, "static LDS of the decode kernel");
 
   // ---- prefix sum of tile counts (every work-group derives the same list)
   const int per = (B + kThreads - 1) / kThreads;
@@ -215,6 +218,7 @@ void decode_sk_kernel(SkParams p) {
   __syncthreads();
   const int ntiles = s_cu[B];
   const int R = min(p.ranges, ntiles);  // ranges in use: none of them is empty
+  if (blockIdx.x == 0 && tid == 0) p.ws_status[0] = kStatusOk;  // the merge kernel runs after this launch
   if (hg == 0 && tid == 0) {
     // the merge kernel's work list: the sequence cut at this range's start, if this is the
     // first range boundary inside it, with the ranges that hold its first and last tiles
@@ -709,18 +713,25 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
       __hip_atomic_store(&s_ready[hw * kRows + pw], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     } else {
       // the other rows of the same work-group always set their flags; the cap only bounds the
-      // wait.  Their results are folded in row order: a fixed order.
+      // wait, and a wait that reaches it leaves kStatusWaitGaveUp in the status word (the row's
+      // partial result is then not trusted by the caller).  Results are folded in row order: a
+      // fixed order.
+      bool gave_up = false;
       for (int j = 1; j < kRows; ++j) {
-        for (int spin = 0; spin < (1 << 22) &&
-                           __hip_atomic_load(&s_ready[hw * kRows + j], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
-             ++spin)
+        int spin = 0;
+        while (spin < p.spin_limit &&
+               __hip_atomic_load(&s_ready[hw * kRows + j], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
           __builtin_amdgcn_s_sleep(1);
+          ++spin;
+        }
+        gave_up = gave_up || spin >= p.spin_limit;
         float2 mlj[1] = {s_ml(j)[lane]};
         f32x4 xj[1][NC];
 #pragma unroll
         for (int q = 0; q < NC; ++q) xj[0][q] = s_a(j)[q * 64 + lane];
         fold_records<1, NC>(m, l, a, mlj, xj, 1);
       }
+      if (gave_up && lane == 0) p.ws_status[0] = kStatusWaitGaveUp;
       if (live && r16 < G) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const int64_t orow = static_cast<int64_t>(s) * p.num_q_heads + g * G + r16;
@@ -805,7 +816,15 @@ int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_le
 }
 
 int sk_lds_bytes_host(int32_t num_seqs, int32_t head_dim, int32_t group) {
-  return sk_lds_bytes(num_seqs, head_dim, group);
+  return sk_lds_bytes(num_seqs, head_dim, group) + kSkStaticLds;
+}
+
+bool sk_fits(int32_t num_seqs, int32_t head_dim, int32_t group) {
+  if (num_seqs < 0 || num_seqs > kSkMaxSeqs || group < 1 || group > 16) return false;
+  if (head_dim != 64 && head_dim != 128) return false;
+  const int heads = sk_heads(num_seqs);
+  return sk_lds_bytes_host(num_seqs, head_dim, group) <= kLdsPerWorkgroup &&
+         merge_lds_bytes(head_dim, heads) + static_cast<int>(kWaves * sizeof(int)) <= kLdsPerWorkgroup;
 }
 
 size_t sk_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len) {
@@ -814,7 +833,7 @@ size_t sk_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_d
   const size_t acc = static_cast<size_t>(recs) * 16 * head_dim * sizeof(float);
   const size_t ml = static_cast<size_t>(recs) * 32 * sizeof(float);
   const size_t desc = static_cast<size_t>(R) * 4 * sizeof(int32_t);
-  return acc + ml + desc;
+  return kStatusBytes + acc + ml + desc;
 }
 
 hipError_t sk_launch(SkParams p, int32_t dtype, hipStream_t stream) {

@@ -11,8 +11,18 @@ namespace sk {
 
 // Waves the work is spread over (about 8 per CU on a 256-CU MI355X).
 constexpr int kSkTargetWaves = 2048;
+// Bytes reserved at the start of the workspace for the status word (records follow, aligned).
+constexpr int kStatusBytes = 256;
+// Status word values.
+constexpr int32_t kStatusOk = 0;
+constexpr int32_t kStatusWaitGaveUp = 1;
+// Default poll count of the merge kernel's waits on LDS flags: far beyond what co-resident
+// waves of one work-group ever need, and still a bounded wait.
+constexpr int32_t kDefaultSpinLimit = 1 << 22;
 // Largest batch the path takes (the prefix sum of block counts lives in LDS).
 constexpr int kSkMaxSeqs = 8192;
+// LDS one work-group may hold on gfx950 (the whole 160 KiB of a CU).
+constexpr int kLdsPerWorkgroup = 160 * 1024;
 
 struct SkParams {
   void* out;
@@ -27,6 +37,10 @@ struct SkParams {
   float* ws_ml;      // [ranges][Hkv][2][16][2]  (running max, sum); ranges are per work-group
   int32_t* ws_desc;  // [ranges][4] per range: the sequence cut at its start whose merge it owns
                      // (or -1), with the first and last range holding tiles of that sequence
+  int32_t* ws_status;  // one word at the start of the workspace: cleared by the decode kernel, set
+                       // to kStatusWaitGaveUp by the merge kernel if one of its bounded waits ended
+                       // without the flag it waited for
+  int32_t spin_limit;  // polls of such a wait before it gives up
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -54,8 +68,13 @@ struct SkParams {
 inline int32_t sk_heads(int32_t num_seqs) { return num_seqs < 8 ? 1 : 4; }
 // Ranges per KV head for these arguments (host).
 int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len);
-// LDS bytes of the decode kernel for these shapes (host); above 64 KiB needs no opt-in here.
+// LDS bytes of the decode kernel for these shapes (host), dynamic and static together;
+// above 64 KiB needs no opt-in here.
 int sk_lds_bytes_host(int32_t num_seqs, int32_t head_dim, int32_t group);
+// Whether the path's kernels fit one work-group's LDS for these shapes (host).  The prefix
+// sum takes about 8 bytes per sequence and the wave states 2 * 8 * group * head_dim * 4, so
+// large batches with large groups do not fit (group 16, head_dim 128: up to 3807 sequences).
+bool sk_fits(int32_t num_seqs, int32_t head_dim, int32_t group);
 // Workspace bytes the path needs (host).
 size_t sk_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len);
 // Enqueues the decode kernel and the merge kernel on `stream`.

@@ -333,26 +333,70 @@ def test_workspace_size_and_partition_rules():
     assert ps(64, 32, 32, 128, 8192, 0, "float16") == 0 and ws(64, 32, 32, 128, 8192, 0, "float16") > 0
     assert ws(64, 32, 32, 128, 8192, 0, 7) == 0 and ps(64, 32, 32, 128, 8192, 0, 7) == 0  # unknown dtype
     # auto with 16-bit pools: the even split over the GPU has no fixed partition; its workspace
-    # holds, per work range, records (16 x D fp32 acc + 16 x 2 stats, two per KV head) and
-    # one 16-byte descriptor
+    # holds a 256-byte status area, then, per work range, records (16 x D fp32 acc + 16 x 2
+    # stats, two per KV head) and one 16-byte descriptor
     assert ps(256, 64, 8, 128, 8192, 0) == 0
-    w128 = ws(256, 64, 8, 128, 8192, 0)
-    w64 = ws(256, 64, 8, 64, 8192, 0)
+    status = 256
+    w128 = ws(256, 64, 8, 128, 8192, 0) - status
+    w64 = ws(256, 64, 8, 64, 8192, 0) - status
     rec128, rec64 = 16 * 128 * 4 + 32 * 4, 16 * 64 * 4 + 32 * 4
     per_range128, per_range64 = 2 * 8 * rec128 + 16, 2 * 8 * rec64 + 16
     assert w128 > 0 and w128 % per_range128 == 0 and w64 % per_range64 == 0
     assert w128 // per_range128 == w64 // per_range64  # same number of ranges
-    assert ws(256, 64, 8, 128, 8192, 0) == w128  # deterministic
+    assert ws(256, 64, 8, 128, 8192, 0) - status == w128  # deterministic
     # small batches: one range per 8 worst-case tiles (4 x 1024 tokens: 256 tiles -> 32 ranges),
     # large ones: about 2048 waves (8 per work-group, 4 KV heads each -> 128 ranges at 8 KV heads)
-    assert ws(4, 64, 8, 128, 1024, 0) == 32 * per_range128
-    assert ws(256, 64, 8, 128, 8192, 0) == 128 * per_range128
+    assert ws(4, 64, 8, 128, 1024, 0) == status + 32 * per_range128
+    assert ws(256, 64, 8, 128, 8192, 0) == status + 128 * per_range128
     # tiny contexts: at most one range per 8 worst-case tiles
-    assert ws(1, 8, 1, 128, 16, 0) <= 2 * rec128 + 256
+    assert ws(1, 8, 1, 128, 16, 0) <= status + 2 * rec128 + 256
     assert ws(0, 64, 8, 128, 8192, 0) == 0
     # beyond the even split's batch limit the fixed rule applies again
     big = ps(9000, 64, 8, 128, 8192, 0)
     assert big % 16 == 0 and big > 0
+
+
+# LDS of the even split's decode work-group: the prefix sum of tile counts (lengths and
+# suffix starts, each array rounded up to 16 bytes), then the larger of the 8 waves' V tiles
+# (16 rows at a pitch of 288 bytes for D 128, 160 for D 64) and the 8 waves' two states
+# (G rows of D fp32 plus (m, l) per row, rounded up to 16 bytes), plus 256 bytes of static LDS.
+def _sk_lds(b, d, g):
+    up16 = lambda x: -(-x // 16) * 16
+    tiles = 8 * 16 * (288 if d == 128 else 160)
+    states = 2 * 8 * up16((d // 16) * 4 * g * 16 + g * 8)
+    return up16((b + 1) * 4) + up16(b * 4) + max(tiles, states) + 256
+
+
+@pytest.mark.parametrize("g,d", [(16, 128), (13, 128), (12, 128), (16, 64), (8, 128), (1, 128)])
+def test_even_split_is_taken_only_where_its_lds_fits(g, d):
+    """The even split keeps a prefix sum of every sequence's tile count and 16 wave states in
+    one work-group's LDS (160 KiB on gfx950).  Batches whose state does not fit take fixed
+    partitions (partition size > 0, the fixed workspace), and the prefix-shared decode, which
+    needs the even split, reports no workspace; at the largest batch that fits, the even split
+    is still taken."""
+    ws = B.paged_attn_workspace_bytes
+    ps = B.paged_attn_partition_size
+    pws = B.paged_attn_decode_prefix_workspace_bytes
+    hkv = 2
+    hq = g * hkv
+    fits = [b for b in range(1, 8193) if _sk_lds(b, d, g) <= 160 * 1024]
+    largest = fits[-1] if fits else 0
+    for b in {1, 7, 8, 1000, 3804, 3805, 3815, 6919, 6920, 7975, 7976, 8192, largest, min(largest + 1, 8192)}:
+        even = b in fits
+        assert (ps(b, hq, hkv, d, 512, 0, "bfloat16") == 0) == even, (b, g, d)
+        if even:
+            assert ws(b, hq, hkv, d, 512, 0, "bfloat16") > 0
+            assert pws(b, hq, hkv, d, 512, 256, "bfloat16") > 0
+        else:
+            assert ps(b, hq, hkv, d, 512, 0, "bfloat16") == 512
+            assert ws(b, hq, hkv, d, 512, 0, "bfloat16") == 0  # one partition: nothing to merge
+            assert ws(b, hq, hkv, d, 4096, 0, "bfloat16") == b * hq * 8 * (d + 2) * 4
+            assert pws(b, hq, hkv, d, 512, 256, "bfloat16") == 0
+    if g == 16 and d == 128:
+        assert largest == 3807
+        assert ps(8192, hq, hkv, d, 512, 0, "bfloat16") > 0
+    if g <= 8:
+        assert largest == 8192
 
 
 def test_prefix_workspace_size():
