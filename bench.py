@@ -376,6 +376,201 @@ def bench_append(args, dev):
                          "bytes_per_launch": moved, "avg_launch_us": round(t * 1e6, 2)}}
 
 
+def fused_append_bytes(w):
+    """Bytes the fused call moves for its append beyond the decode's own: each sequence's new K
+    and V rows are read as part of its context (counted in the K/V bytes) and written once to
+    their pool slots."""
+    sp = w.spec
+    e = {"float32": 4, "float16": 2, "bfloat16": 2}[sp.dtype]
+    return 2 * sp.num_seqs * sp.num_kv_heads * sp.head_dim * e
+
+
+def append_call_bytes(w):
+    """Bytes of the append as a call of its own (pkv_kv_cache_append): the new K and V rows read
+    from the input and written to the pools, and the 8-byte slots."""
+    return 2 * fused_append_bytes(w) + 8 * w.spec.num_seqs
+
+
+def measure_step(w, dev, steps, warmup, partition=0, mode="fused"):
+    """Builds the workload's pools, lets the host pool take each sequence's next slot, and times
+    the decode step of `mode`:
+      fused    one pkv_paged_attn_decode_append call (the default step);
+      separate pkv_kv_cache_append, then pkv_paged_attn_decode;
+      prefix   pkv_kv_cache_append, then pkv_paged_attn_decode_prefix (groups from the pool).
+    K steps run back to back between two HIP events on the launch stream (after W warm-up
+    steps); a second pass of K steps puts events around every call for the per-call times.  The
+    append call is also timed on its own.  Returns the times and the byte counts."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_376_amd import binding
+    from paged_kv_cache_376_amd.cache import build_cache
+
+    sp = w.spec
+    t0 = time.perf_counter()
+    cache = build_cache(w, dev)
+    torch.cuda.synchronize()
+    log(f"{sp.name}: pool built in {time.perf_counter() - t0:.1f} s ({w.num_blocks} blocks)")
+    seqs = list(range(sp.num_seqs))
+    # Host side of the step, done once: every sequence takes the slot of its next token.
+    slots = np.zeros(sp.num_seqs, dtype=np.int64)
+    for i, s in enumerate(seqs):
+        sl, cow = cache.pool.seq_extend(s, 1)
+        cache.copy_blocks(cow)
+        slots[i] = sl[0]
+    slot_t = torch.from_numpy(slots).to(dev)
+    new_k = w.new_k.to(dev).contiguous()
+    new_v = w.new_v.to(dev).contiguous()
+    bt, ctx, maxc = cache.tables(seqs)
+    q = w.q.to(dev).contiguous()
+    out = torch.empty_like(q)
+    part = binding.paged_attn_partition_size(sp.num_seqs, sp.num_q_heads, sp.num_kv_heads,
+                                             sp.head_dim, maxc, partition, sp.dtype)
+    ws_bytes = binding.paged_attn_workspace_bytes(sp.num_seqs, sp.num_q_heads, sp.num_kv_heads,
+                                                  sp.head_dim, maxc, partition, sp.dtype)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def append_call():
+        binding.kv_cache_append(new_k, new_v, cache.k_cache, cache.v_cache, slot_t, stream=stream)
+
+    def decode_call():
+        binding.paged_attn_decode(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale,
+                                  workspace=ws, partition_size=partition, stream=stream)
+
+    def fused_call():
+        binding.paged_attn_decode_append(out, q, new_k, new_v, cache.k_cache, cache.v_cache, bt, ctx,
+                                         maxc, w.scale, workspace=ws, partition_size=partition,
+                                         stream=stream)
+
+    groups = None
+    if mode == "prefix":
+        sp_, offs_, mem_, mx_ = cache.pool.prefix_groups(seqs)
+        groups = (sp_, offs_, mem_, mx_)
+        to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+        sp_d, offs_d, mem_d = to_dev(sp_), to_dev(offs_), to_dev(mem_)
+        pws = binding.paged_attn_decode_prefix_workspace_bytes(sp.num_seqs, sp.num_q_heads, sp.num_kv_heads,
+                                                               sp.head_dim, maxc, mx_, sp.dtype)
+        pws_t = torch.empty(max(pws, 16), dtype=torch.uint8, device=dev)
+        log(f"prefix groups: {len(offs_) - 1}, longest shared prefix {mx_} tokens")
+
+        def prefix_call():
+            binding.paged_attn_decode_prefix(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale, sp_d,
+                                             offs_d, mem_d, mx_, workspace=pws_t, stream=stream)
+
+    calls = {"prefix": lambda: [append_call, prefix_call], "separate": lambda: [append_call, decode_call],
+             "fused": lambda: [fused_call]}[mode]()
+    log(f"{sp.name}: warmup {warmup} steps ({mode}, partition {part or 'even split'}, workspace {ws_bytes} B)")
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps back to back, bracketed by synchronize + events on the launch stream.
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        for c in calls:
+            c()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / steps
+    # Per-call durations for the roofline record: a second pass of K steps with HIP events on
+    # the launch stream around every call (kept out of the step timing above).
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for j, c in enumerate(calls):
+            c()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    t_calls = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(len(calls))] for i in range(steps)])
+    t_dec = t_calls[:, -1]
+    t_app = t_calls[:, 0] if mode != "fused" else None
+    # the append alone, back to back (it rewrites the same rows into the same slots)
+    append_us = _time_calls(append_call, steps, warmup, stream) * 1e6
+    if mode == "fused":
+        log(f"{sp.name}: step {ms_step * 1e3:.1f} us: fused append+decode call median {np.median(t_dec) * 1e3:.1f} "
+            f"us (p10 {np.percentile(t_dec, 10) * 1e3:.1f}, p90 {np.percentile(t_dec, 90) * 1e3:.1f}); "
+            f"append alone {append_us:.1f} us")
+    else:
+        log(f"{sp.name}: step {ms_step * 1e3:.1f} us: append {t_app.mean() * 1e3:.1f} us, decode "
+            f"median {np.median(t_dec) * 1e3:.1f} us (p10 {np.percentile(t_dec, 10) * 1e3:.1f}, "
+            f"p90 {np.percentile(t_dec, 90) * 1e3:.1f})")
+
+    kv_bytes, dec_bytes = algorithmic_bytes(w)
+    kv_read = kv_bytes
+    if mode == "prefix":
+        # the method reads each shared prefix once per group: that is the roofline's byte count
+        kv_read, dec_bytes = prefix_shared_bytes(w, *groups[:3])
+    if mode == "fused":
+        dec_bytes += fused_append_bytes(w)
+    del cache, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"ms_step": ms_step, "t_dec": t_dec, "t_app": t_app, "append_us": append_us, "part": part,
+            "ws_bytes": ws_bytes, "kv_bytes": kv_bytes, "kv_read": kv_read, "dec_bytes": dec_bytes,
+            "groups": groups}
+
+
+def _config_record(w, m, mode):
+    """One per_config entry from measure_step's result."""
+    import numpy as np
+
+    dec_s = float(m["t_dec"].mean()) / 1e3
+    step_s = m["ms_step"] / 1e3
+    achieved = m["dec_bytes"] / dec_s / 1e9
+    sp = w.spec
+    rec = {
+        "workload": f"{sp.name}: B={sp.num_seqs}, Hq={sp.num_q_heads}, Hkv={sp.num_kv_heads}, D={sp.head_dim}, "
+                    f"{sp.dtype}, block {sp.block_size}, lengths {sp.lengths}, +1 appended token per sequence",
+        "step_calls": {"fused": "pkv_paged_attn_decode_append",
+                       "separate": "pkv_kv_cache_append + pkv_paged_attn_decode",
+                       "prefix": "pkv_kv_cache_append + pkv_paged_attn_decode_prefix"}[mode],
+        "step_us": round(m["ms_step"] * 1e3, 2),
+        "kv_bytes_per_step": m["kv_bytes"],
+        "kv_gbs": round(m["kv_bytes"] / step_s / 1e9, 2),
+        "pct_hbm_peak": round(100.0 * m["kv_read"] / step_s / 1e9 / HBM_PEAK_GBS, 2),
+        "decode_us_median": round(float(np.median(m["t_dec"])) * 1e3, 2),
+        "decode_roofline_frac": round(achieved / HBM_PEAK_GBS, 4),
+        "decode_bytes_per_launch": m["dec_bytes"],
+        "append_us": round(m["append_us"], 2),
+        "decode_tokens_per_s_per_layer": round(sp.num_seqs / step_s, 1),
+        "partition_tokens": m["part"] if m["part"] else "even split over the GPU",
+    }
+    if mode == "prefix":
+        rec["kv_bytes_read_per_step"] = m["kv_read"]
+        rec["note"] = ("pct_hbm_peak and the roofline count each group's shared prefix once; kv_gbs counts every "
+                       "sequence's whole context")
+    if sp.name == "tiny_fp32":
+        rec["note"] = "latency-bound (309 KB of K/V); a correctness case"
+    return rec
+
+
+def per_config_records(w_head, head, dev, args):
+    """Every workload the benchmark knows, timed the same way as the headline step (fused call,
+    seed args.seed): the headline's own numbers for gqa_bf16, and for prefix_bf16 also the
+    prefix-shared call."""
+    from paged_kv_cache_376_amd import workloads
+
+    recs = {"gqa_bf16": {
+        "workload": head["config"]["workload"], "step_calls": "pkv_paged_attn_decode_append",
+        "step_us": round(head["ms_per_step"] * 1e3, 2), "kv_bytes_per_step": head["config"]["kv_bytes_per_step"],
+        "kv_gbs": head["value"], "pct_hbm_peak": head["pct_hbm_peak"], "decode_us_median": head["decode_us_median"],
+        "decode_roofline_frac": head["roofline"]["frac"], "decode_bytes_per_launch": head["roofline"]["bytes_per_launch"],
+        "append_us": head["append_us"], "decode_tokens_per_s_per_layer": head["decode_tokens_per_s_per_layer"],
+        "partition_tokens": head["config"]["partition_tokens"]}}
+    for name, mode in (("tiny_fp32", "fused"), ("mha_fp16", "fused"), ("long_bf16", "fused"),
+                       ("prefix_bf16", "fused"), ("prefix_bf16", "prefix")):
+        w = workloads.make_workload(name, args.seed)
+        m = measure_step(w, dev, args.steps, args.warmup, 0, mode)
+        recs[name if mode == "fused" else name + "_shared"] = _config_record(w, m, mode)
+    return recs
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -388,6 +583,8 @@ def main():
                     help="time the step as two calls (pkv_kv_cache_append, then "
                          "pkv_paged_attn_decode) instead of one pkv_paged_attn_decode_append")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the per_config record (the other workloads, each timed the same way)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -413,7 +610,6 @@ def main():
     import torch
 
     from paged_kv_cache_376_amd import binding, workloads
-    from paged_kv_cache_376_amd.cache import build_cache
 
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a HIP device")
@@ -429,113 +625,14 @@ def main():
     w = workloads.make_workload(args.config, args.seed,
                                 **({"block_size": args.block_size} if args.block_size else {}))
     sp = w.spec
-    t0 = time.perf_counter()
-    cache = build_cache(w, dev)
-    torch.cuda.synchronize()
-    log(f"pool built in {time.perf_counter() - t0:.1f} s ({w.num_blocks} blocks)")
-
-    seqs = list(range(sp.num_seqs))
-    # Host side of the step, done once: every sequence takes the slot of its next token.
-    slots = np.zeros(sp.num_seqs, dtype=np.int64)
-    for i, s in enumerate(seqs):
-        sl, cow = cache.pool.seq_extend(s, 1)
-        cache.copy_blocks(cow)
-        slots[i] = sl[0]
-    slot_t = torch.from_numpy(slots).to(dev)
-    new_k = w.new_k.to(dev).contiguous()
-    new_v = w.new_v.to(dev).contiguous()
-    bt, ctx, maxc = cache.tables(seqs)
-    q = w.q.to(dev).contiguous()
-    out = torch.empty_like(q)
-    part = binding.paged_attn_partition_size(sp.num_seqs, sp.num_q_heads, sp.num_kv_heads,
-                                             sp.head_dim, maxc, args.partition, sp.dtype)
-    ws_bytes = binding.paged_attn_workspace_bytes(sp.num_seqs, sp.num_q_heads, sp.num_kv_heads,
-                                                  sp.head_dim, maxc, args.partition, sp.dtype)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def append_call():
-        binding.kv_cache_append(new_k, new_v, cache.k_cache, cache.v_cache, slot_t, stream=stream)
-
-    def decode_call():
-        binding.paged_attn_decode(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale,
-                                  workspace=ws, partition_size=args.partition, stream=stream)
-
-    if args.prefix_shared:
-        sp_, offs_, mem_, mx_ = cache.pool.prefix_groups(seqs)
-        to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
-        sp_d, offs_d, mem_d = to_dev(sp_), to_dev(offs_), to_dev(mem_)
-        pws = binding.paged_attn_decode_prefix_workspace_bytes(sp.num_seqs, sp.num_q_heads, sp.num_kv_heads,
-                                                               sp.head_dim, maxc, mx_, sp.dtype)
-        pws_t = torch.empty(max(pws, 16), dtype=torch.uint8, device=dev)
-        log(f"prefix groups: {len(offs_) - 1}, longest shared prefix {mx_} tokens")
-
-    def prefix_call():
-        binding.paged_attn_decode_prefix(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale, sp_d, offs_d,
-                                         mem_d, mx_, workspace=pws_t, stream=stream)
-
-    def fused_call():
-        binding.paged_attn_decode_append(out, q, new_k, new_v, cache.k_cache, cache.v_cache, bt, ctx,
-                                         maxc, w.scale, workspace=ws, partition_size=args.partition,
-                                         stream=stream)
-
-    calls = ([append_call, prefix_call] if args.prefix_shared else
-             [append_call, decode_call] if args.separate else [fused_call])
-    two_calls = args.separate or args.prefix_shared
-    log(f"warmup {args.warmup} steps ({'append + decode' if two_calls else 'fused append+decode'}, "
-        f"partition {part or 'even split'}, workspace {ws_bytes} B)")
-    for _ in range(args.warmup):
-        for c in calls:
-            c()
-    torch.cuda.synchronize()
-
-    # Timed region: K steps back to back, bracketed by synchronize + events on the launch stream.
-    K = args.steps
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(K):
-        for c in calls:
-            c()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / K
-    # Per-call durations for the roofline record: a second pass of K steps with HIP events on
-    # the launch stream around every call (kept out of the step timing above).
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        ev[i][0].record(stream)
-        for j, c in enumerate(calls):
-            c()
-            ev[i][j + 1].record(stream)
-    torch.cuda.synchronize()
-    t_calls = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(len(calls))] for i in range(K)])
-    t_dec = t_calls[:, -1]
-    t_app = t_calls[:, 0] if two_calls else None
-    if two_calls:
-        log(f"step {ms_step * 1e3:.1f} us: append {t_app.mean() * 1e3:.1f} us, decode "
-            f"median {np.median(t_dec) * 1e3:.1f} us (p10 {np.percentile(t_dec, 10) * 1e3:.1f}, "
-            f"p90 {np.percentile(t_dec, 90) * 1e3:.1f})")
-    else:
-        log(f"step {ms_step * 1e3:.1f} us: fused append+decode call median {np.median(t_dec) * 1e3:.1f} us "
-            f"(p10 {np.percentile(t_dec, 10) * 1e3:.1f}, p90 {np.percentile(t_dec, 90) * 1e3:.1f})")
-
-    kv_bytes, dec_bytes = algorithmic_bytes(w)
-    kv_read = kv_bytes
-    if args.prefix_shared:
-        # the method reads each shared prefix once per group: that is the roofline's byte count
-        kv_read, dec_bytes = prefix_shared_bytes(w, sp_, offs_, mem_)
-    e_bytes = {"float32": 4, "float16": 2, "bfloat16": 2}[sp.dtype]
-    app_bytes = 4 * sp.num_seqs * sp.num_kv_heads * sp.head_dim * e_bytes  # new rows read + written
-    if not two_calls:
-        dec_bytes += app_bytes
+    mode = "prefix" if args.prefix_shared else "separate" if args.separate else "fused"
+    m = measure_step(w, dev, args.steps, args.warmup, args.partition, mode)
+    ms_step, t_dec, t_app, part = m["ms_step"], m["t_dec"], m["t_app"], m["part"]
+    kv_bytes, kv_read, dec_bytes = m["kv_bytes"], m["kv_read"], m["dec_bytes"]
+    two_calls = mode != "fused"
     dec_s = float(t_dec.mean()) / 1e3
     gbs = kv_bytes / (ms_step / 1e3) / 1e9
     achieved = dec_bytes / dec_s / 1e9
-
     if args.copy_calibration:
         n = 1 << 30
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -550,7 +647,7 @@ def main():
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
@@ -563,9 +660,11 @@ def main():
         "pct_hbm_peak": round(100.0 * kv_read / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s_per_layer": round(sp.num_seqs / (ms_step / 1e3), 1),
         "decode_tokens_per_s_70b_shape_attention_only": round(sp.num_seqs / (LAYERS_70B * ms_step / 1e3), 1),
-        "append_us": None if t_app is None else round(float(t_app.mean()) * 1e3, 2),
-        # the append's algorithmic bytes (new rows read and written, 8-byte slots) over its time
-        "append_gbs": None if t_app is None else round((app_bytes + 8 * sp.num_seqs) / (float(t_app.mean()) / 1e3) / 1e9, 2),
+        # pkv_kv_cache_append of the step's new rows, timed on its own (the fused call does the
+        # same writes inside the decode): mean time per call and its algorithmic bytes (new rows
+        # read and written, 8-byte slots) over that time
+        "append_us": round(m["append_us"], 2),
+        "append_gbs": round(append_call_bytes(w) / (m["append_us"] / 1e6) / 1e9, 2),
         "decode_us_median": round(float(np.median(t_dec)) * 1e3, 2),
         "decode_us_p10": round(float(np.percentile(t_dec, 10)) * 1e3, 2),
         "decode_us_p90": round(float(np.percentile(t_dec, 90)) * 1e3, 2),
@@ -598,7 +697,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             # counters were taken on the default workload with the fused call
             "traffic": counter_traffic() if (args.config == "gqa_bf16" and args.seed == 0 and not two_calls
-                                             and args.partition == 0) else None,
+                                             and args.partition == 0 and not args.block_size) else None,
             "bytes_per_launch": dec_bytes,
             "avg_launch_us": round(dec_s * 1e6, 2),
         },
@@ -609,6 +708,10 @@ def main():
             f"({100 * ceiling['frac_of_peak']:.1f}% of {HBM_PEAK_GBS:.0f})")
         result["read_ceiling"] = ceiling
         result["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["value"], 4)
+    if not args.no_per_config and args.config == "gqa_bf16" and mode == "fused" and not args.block_size \
+            and args.partition == 0:
+        del m
+        result["per_config"] = per_config_records(w, result, dev, args)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

@@ -67,6 +67,23 @@ def oracle_out(w, seqs=None, q=None):
     return oracle.decode_attention(qq, [k for k, _ in kv], [v for _, v in kv], w.scale)
 
 
+_FULL_ORACLE = {}
+
+
+def oracle_full(w, chunk=32):
+    """The oracle over every sequence of a workload, computed a chunk of sequences at a time
+    (so that the fp64 K/V of long contexts is never held for the whole batch) and kept for the
+    session, keyed by the workload's spec and seed: the plain and the fused test of one
+    workload share it."""
+    key = (w.spec, w.seed)
+    if key not in _FULL_ORACLE:
+        B = w.spec.num_seqs
+        parts = [oracle_out(w, range(a, min(B, a + chunk))) for a in range(0, B, chunk)]
+        _FULL_ORACLE.clear()  # one workload at a time: outputs of the largest are 16 MB
+        _FULL_ORACLE[key] = np.concatenate(parts, axis=0)
+    return _FULL_ORACLE[key]
+
+
 def max_err(out, ref) -> float:
     got = out.double().numpy()
     return float(np.max(np.abs(got - ref))) if got.size else 0.0
@@ -75,3 +92,25 @@ def max_err(out, ref) -> float:
 def bits(t: torch.Tensor) -> torch.Tensor:
     """Raw bit pattern of a tensor, for bitwise comparisons."""
     return t.view({4: torch.int32, 2: torch.int16}[t.element_size()])
+
+
+def ulp_distance(a: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
+    """Elementwise distance in units in the last place between two tensors of one 16- or
+    32-bit float type: the difference of their positions on the ordered line of that type's
+    values (negative values mirrored below zero, so +0 and -0 coincide)."""
+    def key(t):
+        x = bits(t).to(torch.int64)
+        sign = 1 << (8 * t.element_size() - 1)
+        x = torch.where(x < 0, x + 2 * sign, x)  # unsigned pattern
+        return torch.where(x >= sign, sign - x, x)
+    return (key(a) - key(b)).abs()
+
+
+def within_one_ulp(a: torch.Tensor, b: torch.Tensor, abs_floor: float = 1e-6) -> bool:
+    """Whether two results of one computation that differ only in the rounding order of fp32
+    sums agree after rounding to their 16-bit type: elementwise at most one unit in the last
+    place apart, or, for values so close to zero that the fp32 sums' rounding noise (about
+    1e-8 absolute at the magnitudes of an attention output) spans several of their units,
+    within abs_floor of each other."""
+    near = (a.double() - b.double()).abs() <= abs_floor
+    return bool(((ulp_distance(a, b) <= 1) | near).all())

@@ -30,3 +30,13 @@ def test_prefix_shared_bytes_count_each_prefix_once():
     plain_kv, plain_dec = bench.algorithmic_bytes(w)
     assert plain_kv - kv == 8 * 320 * row  # 11 members read the prefix, 3 reads remain
     assert plain_dec - dec == plain_kv - kv
+
+
+def test_append_bytes_are_counted_once():
+    """The fused call reads each new row as part of its context (already in the K/V bytes) and
+    writes it once; the append as a call of its own reads and writes the rows and reads the
+    8-byte slots."""
+    w = W.make_workload("tiny_fp32", 0)
+    row = 4 * 64 * 4  # Hkv x D x fp32
+    assert bench.fused_append_bytes(w) == 4 * 2 * row  # 4 sequences, K and V written
+    assert bench.append_call_bytes(w) == 4 * 2 * row * 2 + 8 * 4

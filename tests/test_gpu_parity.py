@@ -1,8 +1,9 @@
 """GPU parity of the whole decode step (append + paged decode) against the fp64 oracle.
 
-Small variants of the five workloads are compared element by element; the full-size
-workloads (the shapes and launch configuration the benchmark times) on sampled sequences.
-Pools start filled with NaN, so any read of a slot the step does not own shows up.
+Small variants of the five workloads, and the full-size workloads in the shapes and launch
+configuration the benchmark times, are compared with the oracle element by element over
+every sequence.  Pools start filled with NaN, so any read of a slot the step does not own
+shows up.
 """
 
 import numpy as np
@@ -10,7 +11,7 @@ import pytest
 import torch
 
 from paged_kv_cache_376_amd import workloads as W
-from tests.gpu_common import TOL, decode_step, decode_step_fused, max_err, oracle_out, say
+from tests.gpu_common import TOL, decode_step, decode_step_fused, max_err, oracle_full, oracle_out, say
 
 pytestmark = pytest.mark.gpu
 
@@ -53,22 +54,23 @@ def test_small_gqa_other_seeds(seed):
     assert max_err(out, oracle_out(w)) <= TOL[spec.dtype]
 
 
+def _worst(out, ref):
+    """Max abs error over everything and the sequence where it is reached."""
+    err = np.abs(out.double().numpy() - ref).reshape(ref.shape[0], -1).max(axis=1)
+    return float(err.max()), int(err.argmax())
+
+
 @pytest.mark.parametrize("name", ["mha_fp16", "gqa_bf16", "long_bf16", "prefix_bf16"])
-def test_full_size_sampled(name):
-    """Full workload in the benchmark's launch configuration; sampled sequences checked."""
+def test_full_size_every_sequence(name):
+    """Full workload in the benchmark's launch configuration (append, then the decode with the
+    default work split): every output of every sequence against the oracle."""
     say(f"[parity full] {name}")
     w = W.make_workload(name, 0)
     out, *_ = decode_step(w)
     assert torch.isfinite(out.float()).all()
-    lens = w.context_lens
-    rng = np.random.default_rng(11)
-    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
-    pick |= set(rng.choice(w.spec.num_seqs, size=min(6, w.spec.num_seqs), replace=False).tolist())
-    seqs = sorted(pick)
-    ref = oracle_out(w, seqs)
-    err = max_err(out[seqs], ref)
-    say(f"    sampled seqs {seqs}: max abs err {err:.3e}")
-    assert err <= TOL[w.spec.dtype], err
+    err, s = _worst(out, oracle_full(w))
+    say(f"    {w.spec.num_seqs} sequences: max abs err {err:.3e} (sequence {s})")
+    assert err <= TOL[w.spec.dtype], (err, s)
 
 
 SHAPES = [
@@ -98,22 +100,23 @@ def test_shapes_match_oracle(dtype, hq, hkv, d, lens, partition):
 
 
 @pytest.mark.parametrize("name", ["gqa_bf16", "long_bf16", "prefix_bf16", "mha_fp16"])
-def test_full_size_fused_sampled(name):
+def test_full_size_fused_every_sequence(name):
     """The benchmark's own call (pkv_paged_attn_decode_append, default work split) at full
-    size: every output finite, sampled sequences (longest, shortest, 6 random) against the
-    oracle."""
+    size: every output of every sequence against the oracle, and every appended row in its
+    slot bit for bit."""
     say(f"[parity full fused] {name}")
     w = W.make_workload(name, 0)
-    out, *_ = decode_step_fused(w)
+    out, cache, _, _, _, slots = decode_step_fused(w)
     assert torch.isfinite(out.float()).all()
-    lens = w.context_lens
-    rng = np.random.default_rng(17)
-    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
-    pick |= set(rng.choice(w.spec.num_seqs, size=min(6, w.spec.num_seqs), replace=False).tolist())
-    seqs = sorted(pick)
-    err = max_err(out[seqs], oracle_out(w, seqs))
-    say(f"    sampled seqs {seqs}: max abs err {err:.3e}")
-    assert err <= TOL[w.spec.dtype], err
+    err, s = _worst(out, oracle_full(w))
+    say(f"    {w.spec.num_seqs} sequences: max abs err {err:.3e} (sequence {s})")
+    assert err <= TOL[w.spec.dtype], (err, s)
+    bs = w.spec.block_size
+    sl = torch.from_numpy(slots)
+    k_rows = cache.k_cache[(sl // bs).to(cache.k_cache.device), (sl % bs).to(cache.k_cache.device)].cpu()
+    v_rows = cache.v_cache[(sl // bs).to(cache.v_cache.device), (sl % bs).to(cache.v_cache.device)].cpu()
+    assert torch.equal(k_rows.view(torch.int16), w.new_k.view(torch.int16))
+    assert torch.equal(v_rows.view(torch.int16), w.new_v.view(torch.int16))
 
 
 @pytest.mark.parametrize("as_handle", [False, True])
@@ -142,8 +145,7 @@ def test_decode_on_a_side_stream_with_its_own_workspace(as_handle):
 
 def test_batch_beyond_the_even_split_limit():
     """More than 8192 sequences: the decode takes the fixed-partition path (the even split keeps
-    its prefix sum in LDS up to 8192).  Every output finite; 40 sampled sequences, the longest
-    and the shortest among them, against the oracle."""
+    its prefix sum in LDS up to 8192).  Every output of every sequence against the oracle."""
     say("[parity] 8300 sequences")
     from paged_kv_cache_376_amd import binding
 
@@ -153,20 +155,17 @@ def test_batch_beyond_the_even_split_limit():
     assert binding.paged_attn_partition_size(n, 16, 2, 128, max(lens) + 1, 0, "bfloat16") > 0
     out, *_ = decode_step(w, partition_size=0)
     assert torch.isfinite(out.float()).all()
-    rng = np.random.default_rng(23)
-    seqs = sorted({int(np.argmax(lens)), int(np.argmin(lens))} | set(rng.choice(n, size=38, replace=False).tolist()))
-    err = max_err(out[seqs], oracle_out(w, seqs))
-    say(f"    sampled {len(seqs)} sequences: max abs err {err:.3e}")
-    assert err <= TOL["bfloat16"]
+    err, s = _worst(out, oracle_full(w, chunk=1024))
+    say(f"    {n} sequences: max abs err {err:.3e} (sequence {s})")
+    assert err <= TOL["bfloat16"], (err, s)
 
 
 @pytest.mark.parametrize("fused", [False, True])
 def test_batch_at_the_even_split_limit(fused):
     """Exactly 8192 sequences, the even split's largest batch (its prefix sum of tile counts
     fills the most LDS), G 8, lengths 0-69 so that a range holds many whole sequences and
-    some empty ones.  Every output finite; 40 sampled sequences (the longest and shortest
-    among them) against the oracle; with the fused call, the sampled appended rows in their
-    slots."""
+    some empty ones.  Every output of every sequence against the oracle; with the fused call,
+    every appended row in its slot."""
     say(f"[parity] 8192 sequences, fused={fused}")
     from paged_kv_cache_376_amd import binding
 
@@ -179,17 +178,15 @@ def test_batch_at_the_even_split_limit(fused):
     else:
         out, cache, *_ = decode_step(w)
     assert torch.isfinite(out.float()).all()
-    rng = np.random.default_rng(33)
-    seqs = sorted({int(np.argmax(lens)), int(np.argmin(lens))} | set(rng.choice(n, size=38, replace=False).tolist()))
-    err = max_err(out[seqs], oracle_out(w, seqs))
-    say(f"    sampled {len(seqs)} sequences: max abs err {err:.3e}")
-    assert err <= TOL["bfloat16"]
+    err, s = _worst(out, oracle_full(w, chunk=1024))
+    say(f"    {n} sequences: max abs err {err:.3e} (sequence {s})")
+    assert err <= TOL["bfloat16"], (err, s)
     if fused:
         bs = w.spec.block_size
-        for s in seqs:
-            b, o = int(slots[s]) // bs, int(slots[s]) % bs
-            assert torch.equal(cache.k_cache[b, o].cpu().view(torch.int16), w.new_k[s].view(torch.int16))
-            assert torch.equal(cache.v_cache[b, o].cpu().view(torch.int16), w.new_v[s].view(torch.int16))
+        sl = torch.from_numpy(slots).to(cache.k_cache.device)
+        # sequences with an empty context before the append hold their new token at position 0
+        assert torch.equal(cache.k_cache[sl // bs, sl % bs].cpu().view(torch.int16), w.new_k.view(torch.int16))
+        assert torch.equal(cache.v_cache[sl // bs, sl % bs].cpu().view(torch.int16), w.new_v.view(torch.int16))
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -226,3 +223,51 @@ def test_small_batch_fused_append(n, bs):
         b, o = int(slots[s]) // bs, int(slots[s]) % bs
         assert torch.equal(cache.k_cache[b, o].cpu().view(torch.int16), w.new_k[s].view(torch.int16))
         assert torch.equal(cache.v_cache[b, o].cpu().view(torch.int16), w.new_v[s].view(torch.int16))
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("g", [12, 16])
+@pytest.mark.parametrize("n", [8, 16])
+def test_large_groups_with_four_heads_per_work_group(n, g, fused):
+    """Group sizes above 8 at head_dim 128 with 8 or more sequences: the decode work-groups
+    take 4 KV heads x 2 sub-ranges and the merge kernel folds one record per load over two
+    wave rows.  Contexts of several thousand tokens among short ones are cut into many ranges,
+    so the merge folds long chains.  Plain and fused calls against the oracle; the fused call's
+    appended rows in their slots bit for bit."""
+    lens = tuple(int(x) for x in np.random.default_rng(60 + n + g).integers(1, 6000, size=n))
+    lens = (7000, 3) + lens[2:]
+    say(f"[parity large groups] n={n} G={g} fused={fused} lens={lens}")
+    w = W.Workload(W.Spec("large-g", "bfloat16", n, g * 8, 8, 128, "fixed", fixed_lengths=lens), seed=61 + g)
+    if fused:
+        out, cache, _, _, _, slots = decode_step_fused(w)
+    else:
+        out, *_ = decode_step(w)
+    err = max_err(out, oracle_out(w))
+    say(f"    max abs err {err:.3e}")
+    assert torch.isfinite(out.float()).all() and err <= TOL["bfloat16"], err
+    if fused:
+        for s in range(n):
+            b, o = int(slots[s]) // 16, int(slots[s]) % 16
+            assert torch.equal(cache.k_cache[b, o].cpu().view(torch.int16), w.new_k[s].view(torch.int16))
+            assert torch.equal(cache.v_cache[b, o].cpu().view(torch.int16), w.new_v[s].view(torch.int16))
+
+
+@pytest.mark.parametrize("n", [3807, 4000])
+def test_group_16_at_batches_around_the_lds_limit(n):
+    """Group 16 at head_dim 128: up to 3807 sequences the even split's prefix sum and wave
+    states fit one work-group's LDS and the even split runs; above, the call takes fixed
+    partitions.  Both sides of the limit, plain and fused, against the oracle over every
+    sequence (short contexts, so that a range holds many whole sequences)."""
+    from paged_kv_cache_376_amd import binding
+
+    lens = tuple(int(x) for x in np.random.default_rng(70 + n).integers(0, 80, size=n))
+    w = W.Workload(W.Spec("g16-limit", "bfloat16", n, 32, 2, 128, "fixed", fixed_lengths=lens), seed=71)
+    even = binding.paged_attn_partition_size(n, 32, 2, 128, max(lens) + 1, 0, "bfloat16") == 0
+    say(f"[parity G16 limit] n={n} even split={even}")
+    assert even == (n <= 3807)
+    ref = oracle_full(w, chunk=1024)
+    for fused in (False, True):
+        out = (decode_step_fused(w) if fused else decode_step(w))[0]
+        err, s = _worst(out, ref)
+        say(f"    fused={fused}: max abs err {err:.3e} (sequence {s})")
+        assert torch.isfinite(out.float()).all() and err <= TOL["bfloat16"], (fused, err, s)
