@@ -106,11 +106,40 @@ def ulp_distance(a: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
     return (key(a) - key(b)).abs()
 
 
-def within_one_ulp(a: torch.Tensor, b: torch.Tensor, abs_floor: float = 1e-6) -> bool:
-    """Whether two results of one computation that differ only in the rounding order of fp32
-    sums agree after rounding to their 16-bit type: elementwise at most one unit in the last
-    place apart, or, for values so close to zero that the fp32 sums' rounding noise (about
-    1e-8 absolute at the magnitudes of an attention output) spans several of their units,
-    within abs_floor of each other."""
-    near = (a.double() - b.double()).abs() <= abs_floor
-    return bool(((ulp_distance(a, b) <= 1) | near).all())
+def rounding_bound(q, k, v, scale, dtype):
+    """Elementwise bound [Hq, D] on how far the 16-bit GPU path's output for one sequence
+    (query q [Hq, D], context k, v [L, Hkv, D], all of dtype) may lie from the exact result,
+    from the arithmetic of the MFMA path:
+      * each softmax weight p_t is rounded to the 16-bit type before the PV product, relative to
+        whatever running maximum the wave holds (so the rounding depends on where the context
+        was cut), and the normaliser sums the same rounded weights: a relative error of at most
+        u16 per weight, plus the fp32 error of the logit (D products summed in fp32) carried
+        into the exponent and 4 fp32 ulp for the hardware exp2;
+      * with weights p_t (1 + e_t), out - exact = sum_t p_t e_t (v_t - exact) / sum_t p~_t,
+        at most sum_t p_t |e_t| |v_t - exact| / (sum_t p_t (1 - max|e|));
+      * fp32 sums over the L tokens (products, rescales, merges): L * u32 relative to
+        sum_t p_t (|v_t| + |exact|) / sum_t p_t;
+      * the final rounding to the output type: u16 * |exact|.
+    Two results that may each err by this much differ by at most twice it."""
+    u16 = {"bfloat16": 2.0 ** -8, "float16": 2.0 ** -11}[dtype]
+    u32 = 2.0 ** -24
+    qd = q.double().numpy()
+    kd = k.double().numpy()
+    vd = v.double().numpy()
+    Hq, D = qd.shape
+    L, Hkv, _ = kd.shape
+    G = Hq // Hkv
+    bound = np.zeros((Hq, D))
+    for h in range(Hq):
+        g = h // G
+        z = scale * (kd[:, g, :] @ qd[h])                      # [L] logits
+        w = np.exp(z - z.max())
+        w /= w.sum()
+        exact = w @ vd[:, g, :]                                 # [D]
+        zerr = scale * D * u32 * (np.abs(kd[:, g, :]) @ np.abs(qd[h]))  # logit error, natural-log units
+        eps = u16 + 4 * u32 + zerr                              # [L] relative error of each weight
+        dev = np.abs(vd[:, g, :] - exact)                       # [L, D]
+        weights_term = (w * eps) @ dev / (1.0 - eps.max())
+        sums_term = L * u32 * (w @ np.abs(vd[:, g, :]) + np.abs(exact))
+        bound[h] = weights_term + sums_term + u16 * np.abs(exact) + 1e-7
+    return bound

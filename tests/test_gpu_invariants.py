@@ -12,7 +12,7 @@ import oracle
 from paged_kv_cache_376_amd import workloads as W
 from paged_kv_cache_376_amd.cache import PagedKVCache, build_cache
 from tests.gpu_common import (DEVICE, TOL, bits, decode, decode_step, decode_step_fused, max_err, oracle_out,
-                               say, ulp_distance, within_one_ulp)
+                               rounding_bound, say, ulp_distance)
 
 pytestmark = pytest.mark.gpu
 
@@ -139,24 +139,27 @@ def test_shared_prefix_and_copy_give_identical_outputs(variant):
         # Fixed partitions treat every sequence alike, so equal inputs give equal bits.  The
         # even split over the GPU (partition 0 with f16/bf16 pools) cuts each sequence where
         # the range boundaries happen to fall, so equal sequences at different batch positions
-        # may be merged in a different grouping: their fp32 results differ by rounding only,
-        # and after rounding to the 16-bit output type by at most one unit in the last place.
+        # round their softmax weights against different running maxima: they agree within
+        # twice the rounding bound of the arithmetic (rounding_bound).
         exact = partition != 0 or dtype == "float32"
+        if not exact:
+            bound = torch.from_numpy(2 * rounding_bound(q1[0], k, v, 1.0 / np.sqrt(d), dtype))
         for s in range(1, 5):
             if exact:
                 assert torch.equal(bits(out[s]), bits(out[0])), s
             else:
-                assert within_one_ulp(out[s], out[0]), s
+                assert bool(((out[s].double() - out[0].double()).abs() <= bound).all()), s
 
 
 @pytest.mark.parametrize("dtype", ["bfloat16", "float16"])
-def test_shared_prefix_identity_on_the_even_split_within_one_ulp(dtype):
+def test_shared_prefix_identity_on_the_even_split_within_the_rounding_bound(dtype):
     """I-5 on the default path where the cuts do differ: 24 copies of one 3000-token sequence
     (forks sharing its blocks, and private copies of equal content) among sequences of other
     lengths, so that every copy sits at a different offset of the tile list and is cut at
-    different places.  With the same query every copy gives the same output up to one unit in
-    the last place of the 16-bit type (see within_one_ulp), and most elements agree bit for
-    bit; with fixed partitions every copy agrees bit for bit."""
+    different places.  With the same query every copy lies within the rounding bound of the
+    arithmetic (rounding_bound: 16-bit softmax weights rounded against the running maximum,
+    fp32 sums, final rounding) of the exact result, so any two copies within twice it; with
+    fixed partitions every copy agrees bit for bit."""
     say(f"[inv shared, even split] {dtype}")
     tdt = getattr(torch, dtype)
     hq, hkv, d = 64, 8, 128
@@ -185,14 +188,16 @@ def test_shared_prefix_identity_on_the_even_split_within_one_ulp(dtype):
     bt, ctx, maxc = cache.tables(range(s))
     out = decode(cache, q, bt, ctx, maxc, 1.0 / np.sqrt(d), 0)
     ref = oracle.decode_attention(q1, [k], [v], 1.0 / np.sqrt(d))
+    bound = rounding_bound(q1[0], k, v, 1.0 / np.sqrt(d), dtype)
+    dev = np.stack([np.abs(out[c].double().numpy() - ref[0]) for c in copies])
+    pair = np.stack([np.abs(out[c].double().numpy() - out[copies[0]].double().numpy()) for c in copies])
     ulps = torch.stack([ulp_distance(out[c], out[copies[0]]) for c in copies])
-    same = float((ulps == 0).double().mean())
-    say(f"    max ulp distance {int(ulps.max())}, identical elements {100 * same:.1f}%, "
-        f"max abs err vs oracle {max_err(out[copies], np.repeat(ref, len(copies), axis=0)):.3e}")
-    for c in copies[1:]:
-        assert within_one_ulp(out[c], out[copies[0]]), c
-    assert same >= 0.9
-    assert max_err(out[copies], np.repeat(ref, len(copies), axis=0)) <= TOL[dtype]
+    say(f"    identical elements {100 * float((ulps == 0).double().mean()):.1f}%, max abs err vs oracle "
+        f"{dev.max():.3e} (largest share of the bound {float((dev / bound).max()):.3f}), largest pair "
+        f"difference {pair.max():.3e} (share of twice the bound {float((pair / (2 * bound)).max()):.3f})")
+    assert bool((dev <= bound).all())
+    assert bool((pair <= 2 * bound).all())
+    assert dev.max() <= TOL[dtype]
     fixed = decode(cache, q, bt, ctx, maxc, 1.0 / np.sqrt(d), 64)
     for c in copies[1:]:
         assert torch.equal(bits(fixed[c]), bits(fixed[copies[0]])), c
