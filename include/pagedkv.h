@@ -25,7 +25,9 @@
  *     PyTorch tensors) that must be 16-byte aligned, and a stream (a hipStream_t passed
  *     as void*; NULL is the default stream).  They enqueue and return; errors inside the
  *     kernels are not reported (see each call's device-side contract).
- *   - The library never allocates device memory.
+ *   - The library never allocates device memory (no hipMalloc, no allocating library call):
+ *     workspaces are the caller's, except that pkv_paged_attn_decode_append_noalloc takes its
+ *     workspace from a fixed scratch array compiled into the library (one per GPU).
  *   - Host pool calls are not thread-safe: one owner per pool.
  *   - Supported by the kernels: dtype f32, f16, bf16; head_dim 64 or 128; block_size 16
  *     (decode of f16/bf16 pools also 8 and 32; appends and block copies any block size).
@@ -230,6 +232,38 @@ PKV_API pkv_status pkv_paged_attn_decode_append(void* out, const void* q,
                                         int32_t num_seqs, int32_t num_q_heads, float scale,
                                         void* workspace, size_t workspace_bytes,
                                         int32_t partition_size, void* stream);
+
+/* Allocation-free variant of pkv_paged_attn_decode_append, for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The same append and decode, on the same kernels, with the
+ * workspace taken from a fixed scratch array that the library holds in device memory: one copy
+ * per GPU (pkv_paged_attn_noalloc_scratch_bytes() bytes, 32 MiB), set up on the first call on
+ * that GPU and kept until the process ends.  The call allocates nothing (no hipMalloc, no
+ * library allocation).
+ *
+ * Arguments as for pkv_paged_attn_decode_append, without workspace and workspace_bytes.  The
+ * stream must belong to the current device.  Every call on one GPU uses that GPU's one scratch
+ * array, which keeps the last call's contents (nothing in it needs to start at zero: each call
+ * clears its status word and writes every record before reading it); two calls that overlap on
+ * one GPU (different streams, or different threads) race on it and give undefined results.
+ * The status word of pkv_paged_attn_workspace_bytes lives at the start of the array, out of the
+ * caller's reach.
+ * Errors: as pkv_paged_attn_decode_append; WORKSPACE_TOO_SMALL when the arguments need more
+ * workspace than the scratch array holds (every even-split decode fits; only large
+ * fixed-partition splits, e.g. f32 pools with long contexts and many sequences, do not), with
+ * the sizes in the message; HIP when the scratch array's address cannot be found on the
+ * current device. */
+PKV_API pkv_status pkv_paged_attn_decode_append_noalloc(void* out, const void* q,
+                                                const void* new_key, const void* new_value,
+                                                void* k_cache, void* v_cache,
+                                                const pkv_cache_desc* cache,
+                                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                const int32_t* context_lens, int32_t max_context_len,
+                                                int32_t num_seqs, int32_t num_q_heads, float scale,
+                                                int32_t partition_size, void* stream);
+
+/* Bytes of the scratch array pkv_paged_attn_decode_append_noalloc uses on each GPU. */
+PKV_API size_t pkv_paged_attn_noalloc_scratch_bytes(void);
 
 /* Decode attention with prefix sharing: the same result as pkv_paged_attn_decode (up to
  * rounding), computed so that a prefix shared by a group of sequences is read once per group.

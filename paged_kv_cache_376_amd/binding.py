@@ -50,6 +50,9 @@ SIGNATURES = {
                                             _P, _P, _P, _I32, _I32, _P, ctypes.c_size_t, _P]),
     "pkv_paged_attn_decode_prefix_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_set_merge_spin_limit": (_I32, [_I32]),
+    "pkv_paged_attn_decode_append_noalloc": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32,
+                                                    ctypes.c_float, _I32, _P]),
+    "pkv_paged_attn_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "pkv_pool_create": (_I32, [_I32, _I32, _PI32, ctypes.POINTER(_P)]),
     "pkv_pool_destroy": (None, [_P]),
     "pkv_pool_num_blocks": (_I32, [_P]),
@@ -361,6 +364,37 @@ def paged_attn_decode_append(out, q, new_key, new_value, k_cache, v_cache, block
         ctypes.byref(desc), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
         int(max_context_len), B, Hq, float(scale), _ptr(workspace), ws_bytes, int(partition_size),
         _stream(stream)))
+
+
+def paged_attn_decode_append_noalloc(out, q, new_key, new_value, k_cache, v_cache, block_tables,
+                                     context_lens, max_context_len, scale, partition_size=0, stream=None) -> None:
+    """pkv_paged_attn_decode_append_noalloc: the same step as paged_attn_decode_append with the
+    library's per-GPU scratch array as workspace; nothing is allocated (here or in the library)."""
+    import torch
+
+    _same(out, q, k_cache, v_cache, new_key, new_value)
+    desc = cache_desc(k_cache)
+    B, Hq, D = q.shape
+    if tuple(out.shape) != (B, Hq, D) or D != desc.head_dim:
+        raise ValueError("q/out must be [B, Hq, D] with the cache's D")
+    if tuple(new_key.shape) != (B, desc.num_kv_heads, D) or tuple(new_value.shape) != tuple(new_key.shape):
+        raise ValueError("new_key/new_value must be [B, Hkv, D]")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if not block_tables.is_contiguous() or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be contiguous [B, max_blocks_per_seq]")
+    if context_lens.numel() != B or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous [B]")
+    _on_device(q.device, block_tables, context_lens)
+    _check(lib().pkv_paged_attn_decode_append_noalloc(
+        _ptr(out), _ptr(q), _ptr(new_key), _ptr(new_value), _ptr(k_cache), _ptr(v_cache),
+        ctypes.byref(desc), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        int(max_context_len), B, Hq, float(scale), int(partition_size), _stream(stream)))
+
+
+def noalloc_scratch_bytes() -> int:
+    """pkv_paged_attn_noalloc_scratch_bytes: the per-GPU scratch array's size."""
+    return int(lib().pkv_paged_attn_noalloc_scratch_bytes())
 
 
 # --------------------------------------------------------------------------- host

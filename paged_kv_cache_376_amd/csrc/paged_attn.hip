@@ -38,6 +38,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "device_launch.h"
@@ -864,3 +865,69 @@ extern "C" int32_t pkv_set_merge_spin_limit(int32_t limit) {
   const int32_t v = limit < 0 ? sk::kDefaultSpinLimit : limit;
   return g_merge_spin_limit.exchange(v);
 }
+
+// ------------------------------------------------------------------------------------
+// Allocation-free variant of pkv_paged_attn_decode_append, for callers that cannot allocate
+// device memory (code under HIP graph capture, tight serving loops).  Its workspace is a
+// file-scope device array: one copy per GPU, kept until the process ends.  In host code the
+// array's name is only a stand-in; its device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that address
+// is handed to the kernels.
+// ------------------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = size_t{32} << 20;  // every even-split workspace fits (at most about 17 MB)
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+pkv_status scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail(PKV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_ERR_UNSUPPORTED, "device ordinal %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !ptr)
+      return fail(PKV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(err));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+}  // namespace
+
+extern "C" size_t pkv_paged_attn_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" pkv_status pkv_paged_attn_decode_append_noalloc(void* out, const void* q, const void* new_key,
+                                                           const void* new_value, void* k_cache, void* v_cache,
+                                                           const pkv_cache_desc* cache,
+                                                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                           const int32_t* context_lens, int32_t max_context_len,
+                                                           int32_t num_seqs, int32_t num_q_heads, float scale,
+                                                           int32_t partition_size, void* stream) {
+  clear_error();
+  if (!new_key || !new_value) return fail(PKV_ERR_INVALID_ARGUMENT, "new_key and new_value must not be NULL");
+  if (!cache) return fail(PKV_ERR_INVALID_ARGUMENT, "cache descriptor is NULL");
+  if (num_seqs == 0) return PKV_OK;
+  const size_t need = pkv_paged_attn_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                                                     max_context_len, partition_size, cache->dtype);
+  if (need > kScratchBytes)
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL,
+                "these arguments need a %zu-byte workspace; the allocation-free call has %zu bytes of scratch",
+                need, kScratchBytes);
+  // the workspace query returns 0 for arguments it rejects: those reach the decode's own
+  // validation below without a device query
+  void* ws = nullptr;
+  if (need > 0) {
+    const pkv_status st = scratch_ptr(&ws);
+    if (st != PKV_OK) return st;
+  }
+  return decode_impl(out, q, k_cache, v_cache, cache, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, num_seqs, num_q_heads, scale, ws, need > 0 ? kScratchBytes : 0,
+                     partition_size, stream, new_key, new_value);
+}
+

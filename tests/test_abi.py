@@ -477,3 +477,23 @@ def test_binding_refuses_index_arrays_off_the_launch_device():
     with pytest.raises(ValueError, match="not on"):
         B.paged_attn_decode_prefix(out, q, k, k.clone(), torch.zeros((2, 3), dtype=torch.int32), ctx, 40, 0.125,
                                    grp, torch.zeros(1, dtype=torch.int32, device="meta"), grp, 0)
+
+
+def test_noalloc_decode_rejects_before_touching_the_device():
+    """The allocation-free step refuses arguments whose workspace exceeds its scratch array
+    (a clear WORKSPACE_TOO_SMALL naming both sizes), missing new rows, and a missing
+    descriptor, all on the host; no sequences is a no-op."""
+    lib = B.lib()
+    assert B.noalloc_scratch_bytes() == 32 << 20
+    d = _desc(nb=64, hkv=2, d=128, dt=0)
+    big = lib.pkv_paged_attn_decode_append_noalloc(16, 16, 16, 16, 16, 16, ctypes.byref(d), 16, 1024, 16, 16384,
+                                                   4096, 2, ctypes.c_float(0.1), 16, None)
+    assert big == 5, B.STATUS_NAMES.get(big)
+    msg = lib.pkv_last_error().decode()
+    assert str(32 << 20) in msg and "workspace" in msg
+    assert lib.pkv_paged_attn_decode_append_noalloc(16, 16, None, 16, 16, 16, ctypes.byref(d), 16, 1, 16, 16, 1, 2,
+                                                    ctypes.c_float(0.1), 0, None) == 1
+    assert lib.pkv_paged_attn_decode_append_noalloc(16, 16, 16, 16, 16, 16, None, 16, 1, 16, 16, 1, 2,
+                                                    ctypes.c_float(0.1), 0, None) == 1
+    assert lib.pkv_paged_attn_decode_append_noalloc(16, 16, 16, 16, 16, 16, ctypes.byref(d), 16, 1, 16, 16, 0, 2,
+                                                    ctypes.c_float(0.1), 0, None) == 0
