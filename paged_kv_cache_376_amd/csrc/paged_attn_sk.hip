@@ -155,7 +155,14 @@ __host__ __device__ inline int sk_lds_bytes(int B, int D, int G) {
 
 // SUFFIX: suffix and partial-result mode (seq_start and part_out set), compiled apart so that
 // the plain decode carries none of it.
-template <typename T, int D, int BS, bool SUFFIX, int HEADS>
+// VEC: one query head per KV head (G = 1).  There the tile's products are a 16-token x D
+// matrix-vector product, not a dense contraction, so they run on the vector ALUs: lane
+// (r16, grp) holds token r16's columns 8 (grp + 4c) .. +7 of K, V and q, forms its part of the
+// token's logit with dot2 instructions, sums the four parts over the lane groups, and
+// accumulates weight x its V columns; the weights stay fp32.  At a sequence's end the 16 token
+// lanes of each lane row are summed and the columns moved (through the wave's LDS tile) to the
+// layout of the matrix path, which the rest of the kernel shares.
+template <typename T, int D, int BS, bool SUFFIX, int HEADS, bool VEC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_sk_kernel(SkParams p) {
   constexpr int kHeads = HEADS, kSplits = kWaves / HEADS;
@@ -357,7 +364,8 @@ void decode_sk_kernel(SkParams p) {
         seg_first = (fl & kFirst) != 0;
         seg_k0 = k;
 #pragma unroll
-        for (int c = 0; c < KC; ++c) qb[c] = __builtin_bit_cast(typename M::v8, r16 < G ? qbuf[c] : u32x4{0u, 0u, 0u, 0u});
+        for (int c = 0; c < KC; ++c)
+          qb[c] = __builtin_bit_cast(typename M::v8, (VEC || r16 < G) ? qbuf[c] : u32x4{0u, 0u, 0u, 0u});
         m_run = kNegBig;
         l_run = 0.f;
 #pragma unroll
@@ -373,58 +381,90 @@ void decode_sk_kernel(SkParams p) {
           vbuf[c] = mine ? nv[c] : vbuf[c];
         }
       }
-      // V tile -> LDS (row = token r16), then S^T = K Q^T
+      if constexpr (VEC) {
+        // token r16's logit: this lane's 8 (D / 32) columns, then the sum over the lane groups
+        float dot = 0.f;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) *reinterpret_cast<u32x4*>(vt + r16 * PITCH + (grp + 4 * c) * 16) = vbuf[c];
-      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < KC; ++c) dot = dot8(T{}, kbuf[c], __builtin_bit_cast(u32x4, qb[c]), dot);
+        // this tile's V stays in registers; the next tile's loads go out now
+        u32x4 vcur[KC];
 #pragma unroll
-      for (int c = 0; c < KC; ++c) sacc = M::qk(__builtin_bit_cast(typename M::v8, kbuf[c]), qb[c], sacc);
-      // this tile's registers are consumed: the next tile's loads go out now (none after the
-      // last tile, so that nothing is left in flight when the results are written)
-      if (k + 1 < n) issue(k + 1);
-
-      // online softmax: lane holds tokens 4*grp + e of head r16
-      float sv[4], mx = kNegBig;
+        for (int c = 0; c < KC; ++c) vcur[c] = vbuf[c];
+        if (k + 1 < n) issue(k + 1);
+        dot = swap32_sum(swap16_sum(dot));
+        const float sv = r16 < ntok ? dot * p.scale_log2e : -INFINITY;
+        const float mx = row16_max(sv);  // the tile's maximum (the same in every lane row)
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
+          const float mn = fmaxf(m_run, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+          l_run *= alpha;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sv[e] = (4 * grp + e < ntok) ? sacc[e] * p.scale_log2e : -INFINITY;
-        mx = fmaxf(mx, sv[e]);
-      }
-      mx = swap32_max(swap16_max(mx));
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
-        const float mn = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-        l_run *= alpha;
+          for (int c = 0; c < NC; ++c) acc[c] *= alpha;
+          m_run = mn;
+        }
+        const float pw = __builtin_amdgcn_exp2f(sv - m_run);  // 0 for rows past the context
+        l_run += pw;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc[c] *= alpha;
-        m_run = mn;
-      }
-      i16x4_t pbits;
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const short pe = M::pack(__builtin_amdgcn_exp2f(sv[e] - m_run));
-        pbits[e] = pe;
-        psum += M::unpack(pe);  // the sum uses exactly the rounded weights of the PV product
-      }
-      l_run += psum;
-      wave_lds_sync();
-      if (ntok < kTile) {  // last tile of a sequence: rows past the context may hold anything
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + tr_base + 32 * c));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vb[e] = (4 * grp + e < ntok) ? vb[e] : static_cast<short>(0);
-          acc[c] = M::pv(vb, pbits, acc[c]);
+        for (int c = 0; c < KC; ++c) {
+          float vf[8];
+          unpack(T{}, vcur[c], vf);
+          acc[2 * c] += pw * f32x4{vf[0], vf[1], vf[2], vf[3]};
+          acc[2 * c + 1] += pw * f32x4{vf[4], vf[5], vf[6], vf[7]};
         }
       } else {
+        // V tile -> LDS (row = token r16), then S^T = K Q^T
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + tr_base + 32 * c));
-          acc[c] = M::pv(vb, pbits, acc[c]);
+        for (int c = 0; c < KC; ++c) *reinterpret_cast<u32x4*>(vt + r16 * PITCH + (grp + 4 * c) * 16) = vbuf[c];
+        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) sacc = M::qk(__builtin_bit_cast(typename M::v8, kbuf[c]), qb[c], sacc);
+        // this tile's registers are consumed: the next tile's loads go out now (none after the
+        // last tile, so that nothing is left in flight when the results are written)
+        if (k + 1 < n) issue(k + 1);
+
+        // online softmax: lane holds tokens 4*grp + e of head r16
+        float sv[4], mx = kNegBig;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[e] = (4 * grp + e < ntok) ? sacc[e] * p.scale_log2e : -INFINITY;
+          mx = fmaxf(mx, sv[e]);
         }
+        mx = swap32_max(swap16_max(mx));
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
+          const float mn = fmaxf(m_run, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+          l_run *= alpha;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) acc[c] *= alpha;
+          m_run = mn;
+        }
+        i16x4_t pbits;
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const short pe = M::pack(__builtin_amdgcn_exp2f(sv[e] - m_run));
+          pbits[e] = pe;
+          psum += M::unpack(pe);  // the sum uses exactly the rounded weights of the PV product
+        }
+        l_run += psum;
+        wave_lds_sync();
+        if (ntok < kTile) {  // last tile of a sequence: rows past the context may hold anything
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + tr_base + 32 * c));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vb[e] = (4 * grp + e < ntok) ? vb[e] : static_cast<short>(0);
+            acc[c] = M::pv(vb, pbits, acc[c]);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + tr_base + 32 * c));
+            acc[c] = M::pv(vb, pbits, acc[c]);
+          }
+        }
+        wave_lds_sync();
       }
-      wave_lds_sync();
 
       bool seg_end = (k == n - 1);
       if (!seg_end) {
@@ -432,6 +472,25 @@ void decode_sk_kernel(SkParams p) {
         seg_end = (i2 < 64 ? lane_val(ent.y, i2) : lane_val(ent2.y, i2 - 64)) != s;
       }
       if (!seg_end) continue;
+      if constexpr (VEC) {
+        // sum the 16 token lanes of each lane row, then move row 0's columns to the matrix
+        // layout (lane (r16, grp): columns 16c + 4grp .. +3 in acc[c]) through this wave's tile
+        l_run = row16_sum(l_run);
+        l_run = grp == 0 ? l_run : 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[c][e] = row16_sum(acc[c][e]);
+        float* cols = reinterpret_cast<float*>(vt);
+        if (r16 == 0) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(cols + 8 * (grp + 4 * (c >> 1)) + 4 * (c & 1)) = acc[c];
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[c] = *reinterpret_cast<const f32x4*>(cols + 16 * c + 4 * grp);
+        wave_lds_sync();
+      }
       const float lsum = swap32_sum(swap16_sum(l_run));
       if (seg_first && (fl & kLast)) {  // the whole sequence lies in this wave's sub-range
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
@@ -774,10 +833,18 @@ template <typename T, int D, int BS, int HEADS>
 hipError_t launch(const SkParams& p, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(sk_lds_bytes(p.num_seqs, D, p.group));
   const int hgroups = (p.num_kv_heads + HEADS - 1) / HEADS;
-  if (p.seq_start)
-    hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, true, HEADS>), dim3(p.ranges * hgroups), dim3(kThreads), lds, stream, p);
-  else
-    hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, false, HEADS>), dim3(p.ranges * hgroups), dim3(kThreads), lds, stream, p);
+  const dim3 grid(p.ranges * hgroups), block(kThreads);
+  if (p.group == 1) {
+    if (p.seq_start)
+      hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, true, HEADS, true>), grid, block, lds, stream, p);
+    else
+      hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, false, HEADS, true>), grid, block, lds, stream, p);
+  } else {
+    if (p.seq_start)
+      hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, true, HEADS, false>), grid, block, lds, stream, p);
+    else
+      hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, false, HEADS, false>), grid, block, lds, stream, p);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((merge_sk_kernel<T, D, HEADS>), dim3(p.ranges * hgroups), dim3(kMergeThreads),

@@ -55,6 +55,43 @@ __device__ __forceinline__ float swap32_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// Sum / max over the 16 lanes of each lane row (lanes 16j .. 16j+15), in every lane of the row:
+// quad swaps, then the half-row and row mirrors (DPP, no LDS).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  return x + dpp<0x140>(x);  // row_mirror
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  return fmaxf(x, dpp<0x140>(x));
+}
+
+// Dot product of two 16-byte vectors of 8 elements, accumulated into c in fp32 (v_dot2c).  The
+// pairs are taken as elements of the whole 8-element vector: bit-casting single 32-bit lanes of
+// a u32x4 to 2-element vectors was compiled to four products of lane 0.
+__device__ __forceinline__ float dot8(BF16, u32x4 a, u32x4 b, float c) {
+  const bf16x8 x = __builtin_bit_cast(bf16x8, a), y = __builtin_bit_cast(bf16x8, b);
+  c = __builtin_amdgcn_fdot2_f32_bf16(x.s01, y.s01, c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(x.s23, y.s23, c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(x.s45, y.s45, c, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(x.s67, y.s67, c, false);
+}
+__device__ __forceinline__ float dot8(F16, u32x4 a, u32x4 b, float c) {
+  const f16x8 x = __builtin_bit_cast(f16x8, a), y = __builtin_bit_cast(f16x8, b);
+  c = __builtin_amdgcn_fdot2(x.s01, y.s01, c, false);
+  c = __builtin_amdgcn_fdot2(x.s23, y.s23, c, false);
+  c = __builtin_amdgcn_fdot2(x.s45, y.s45, c, false);
+  return __builtin_amdgcn_fdot2(x.s67, y.s67, c, false);
+}
+
 // Orders one wave's LDS writes before its own later LDS reads (and vice versa).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
