@@ -64,20 +64,27 @@ def prefix_shared_bytes(w, seq_prefix, group_offsets, group_members):
     return kv, kv + qo + tables
 
 
-COUNTERS = os.path.join(ROOT, "profiles", "decode_gqa_bf16_B256_counters.md")
-# sources of the decode and merge kernels the counters were taken on
-SK_SOURCES = [os.path.join(ROOT, "paged_kv_cache_376_amd", "csrc", f)
-              for f in ("paged_attn_sk.hip", "tile_common.h", "stream_k.h", "dtypes.h")]
+# rocprofv3 counter summaries (FETCH_SIZE / WRITE_SIZE, calibrated on a copy of known size) of the
+# decode call of each workload, keyed by (workload, mode), and the kernel sources they were taken on
+_CSRC = os.path.join(ROOT, "paged_kv_cache_376_amd", "csrc")
+SK_SOURCES = [os.path.join(_CSRC, f) for f in ("paged_attn_sk.hip", "tile_common.h", "stream_k.h", "dtypes.h")]
+PREFIX_SOURCES = SK_SOURCES + [os.path.join(_CSRC, f) for f in ("paged_attn_prefix.hip", "prefix.h")]
+COUNTER_FILES = {
+    ("gqa_bf16", "fused"): ("decode_gqa_bf16_B256_counters.md", SK_SOURCES),
+    ("mha_fp16", "fused"): ("decode_mha_fp16_B64_counters.md", SK_SOURCES),
+    ("long_bf16", "fused"): ("decode_long_bf16_B8_counters.md", SK_SOURCES),
+    ("prefix_bf16", "prefix"): ("decode_prefix_bf16_B128_shared_counters.md", PREFIX_SOURCES),
+}
 
 
-def sk_source_sha256():
-    """SHA-256 of the decode and merge kernels' sources with comments and whitespace removed:
-    an edit of a comment does not change what the counters measured, an edit of code does."""
+def source_sha256(files=None):
+    """SHA-256 of kernel sources with comments and whitespace removed: an edit of a comment does
+    not change what the counters measured, an edit of code does."""
     import hashlib
     import re
 
     h = hashlib.sha256()
-    for f in SK_SOURCES:
+    for f in files or SK_SOURCES:
         text = open(f, encoding="utf-8").read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
         text = re.sub(r"//[^\n]*", " ", text)                # line comments
@@ -85,17 +92,19 @@ def sk_source_sha256():
     return h.hexdigest()
 
 
-def counter_traffic():
-    """Calibrated HBM bytes of one decode call from the committed rocprofv3 counter summary,
-    or None when the kernel source has changed since the counters were taken."""
-    import hashlib
+def counter_traffic(config="gqa_bf16", mode="fused"):
+    """Calibrated HBM bytes of one decode call of this workload from its committed rocprofv3
+    counter summary, or None when there is none or the kernel sources have changed since."""
     import re
 
+    entry = COUNTER_FILES.get((config, mode))
+    if entry is None:
+        return None
     try:
-        text = open(COUNTERS, encoding="utf-8").read()
+        text = open(os.path.join(ROOT, "profiles", entry[0]), encoding="utf-8").read()
         want = re.search(r"kernel_source_sha256: ([0-9a-f]{64})", text).group(1)
         value = int(re.search(r"traffic_bytes_per_call: (\d+)", text).group(1))
-        have = sk_source_sha256()
+        have = source_sha256(entry[1])
     except (OSError, AttributeError):
         return None
     return value if have == want else None
@@ -537,6 +546,7 @@ def _config_record(w, m, mode):
         "decode_us_median": round(float(np.median(m["t_dec"])) * 1e3, 2),
         "decode_roofline_frac": round(achieved / HBM_PEAK_GBS, 4),
         "decode_bytes_per_launch": m["dec_bytes"],
+        "decode_traffic_per_launch": counter_traffic(sp.name, mode),
         "append_us": round(m["append_us"], 2),
         "decode_tokens_per_s_per_layer": round(sp.num_seqs / step_s, 1),
         "partition_tokens": m["part"] if m["part"] else "even split over the GPU",
@@ -561,6 +571,7 @@ def per_config_records(w_head, head, dev, args):
         "step_us": round(head["ms_per_step"] * 1e3, 2), "kv_bytes_per_step": head["config"]["kv_bytes_per_step"],
         "kv_gbs": head["value"], "pct_hbm_peak": head["pct_hbm_peak"], "decode_us_median": head["decode_us_median"],
         "decode_roofline_frac": head["roofline"]["frac"], "decode_bytes_per_launch": head["roofline"]["bytes_per_launch"],
+        "decode_traffic_per_launch": head["roofline"]["traffic"],
         "append_us": head["append_us"], "decode_tokens_per_s_per_layer": head["decode_tokens_per_s_per_layer"],
         "partition_tokens": head["config"]["partition_tokens"]}}
     for name, mode in (("tiny_fp32", "fused"), ("mha_fp16", "fused"), ("long_bf16", "fused"),
@@ -695,9 +706,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            # counters were taken on the default workload with the fused call
-            "traffic": counter_traffic() if (args.config == "gqa_bf16" and args.seed == 0 and not two_calls
-                                             and args.partition == 0 and not args.block_size) else None,
+            # counters are taken per workload (seed 0, default block size and split)
+            "traffic": counter_traffic(args.config, mode) if (args.seed == 0 and args.partition == 0
+                                                              and not args.block_size) else None,
             "bytes_per_launch": dec_bytes,
             "avg_launch_us": round(dec_s * 1e6, 2),
         },
