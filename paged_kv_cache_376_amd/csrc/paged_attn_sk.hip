@@ -776,6 +776,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
       // partial result is then not trusted by the caller).  Results are folded in row order: a
       // fixed order.
       bool gave_up = false;
+#pragma unroll 1
       for (int j = 1; j < kRows; ++j) {
         int spin = 0;
         while (spin < p.spin_limit &&
