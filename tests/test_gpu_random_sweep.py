@@ -1,0 +1,111 @@
+"""GPU parity over seeded random points of the argument space, against the fp64 oracle.
+
+Each case draws (from its own seed) the element type, head dim, KV heads, group size, batch,
+length mix (lognormal, uniform, with empty contexts), block size, partition size and whether
+the append is fused into the decode, then compares every output of every sequence with the
+oracle (and, for the fused call, every appended row bit for bit).  A second set draws
+prefix-shared batches (group sizes, prefix lengths that end inside a block, empty suffixes,
+ungrouped sequences) for pkv_paged_attn_decode_prefix.  Sizes stay where the oracle takes a
+second or two.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_376_amd import binding
+from paged_kv_cache_376_amd import workloads as W
+from paged_kv_cache_376_amd.cache import build_cache
+from tests.gpu_common import DEVICE, TOL, decode_step, decode_step_fused, max_err, oracle_out, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw(seed):
+    rng = np.random.default_rng(seed)
+    dtype = rng.choice(["bfloat16", "float16", "float32"], p=[0.5, 0.35, 0.15])
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 3, 4, 5, 8]))
+    g = int(rng.choice([1, 2])) if dtype == "float32" else int(rng.choice([1, 1, 2, 3, 4, 5, 7, 8, 8, 9, 12, 16]))
+    b = int(rng.choice([1, 2, 3, 5, 7, 8, 9, 17, 40, 130, 300]))
+    # about 1.5M (token x KV head) pairs at most, so that the oracle stays fast
+    cap = max(16, min(6000, int(1.5e6 / (b * hkv))))
+    kind = rng.choice(["lognormal", "uniform", "zeros"])
+    if kind == "lognormal":
+        lens = np.clip(np.round(cap / 4 * np.exp(rng.standard_normal(b))), 0, cap)
+    elif kind == "uniform":
+        lens = rng.integers(0, cap + 1, size=b)
+    else:
+        lens = rng.integers(0, cap + 1, size=b) * (rng.random(b) < 0.6)
+    partition = int(rng.choice([0, -1, 16, 48, 256], p=[0.6, 0.1, 0.1, 0.1, 0.1]))
+    bs = 16 if (dtype == "float32" or partition != 0) else int(rng.choice([8, 16, 32]))
+    fused = bool(rng.random() < 0.5)
+    spec = W.Spec(f"rand{seed}", str(dtype), b, g * hkv, hkv, d, "fixed",
+                  fixed_lengths=tuple(int(x) for x in lens), block_size=bs)
+    return spec, partition, fused
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_decode_matches_oracle(seed):
+    spec, partition, fused = _draw(1000 + seed)
+    say(f"[random] seed {seed}: {spec.dtype} D={spec.head_dim} Hkv={spec.num_kv_heads} "
+        f"G={spec.num_q_heads // spec.num_kv_heads} B={spec.num_seqs} bs={spec.block_size} "
+        f"partition={partition} fused={fused} max len={max(spec.fixed_lengths)}")
+    w = W.Workload(spec, seed=seed)
+    if fused:
+        out, cache, _, _, _, slots = decode_step_fused(w, partition_size=partition)
+    else:
+        out, *_ = decode_step(w, partition_size=partition)
+    assert torch.isfinite(out.float()).all()
+    err = max_err(out, oracle_out(w))
+    say(f"    max abs err {err:.3e}")
+    assert err <= TOL[spec.dtype], err
+    if fused:
+        bs = spec.block_size
+        sl = torch.from_numpy(slots).to(cache.k_cache.device)
+        view = {4: torch.int32, 2: torch.int16}[cache.k_cache.element_size()]
+        assert torch.equal(cache.k_cache[sl // bs, sl % bs].cpu().view(view), w.new_k.view(view))
+        assert torch.equal(cache.v_cache[sl // bs, sl % bs].cpu().view(view), w.new_v.view(view))
+
+
+def _draw_prefix(seed):
+    rng = np.random.default_rng(seed)
+    dtype = str(rng.choice(["bfloat16", "float16"]))
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.integers(1, 17))
+    gs = int(rng.choice([2, 3, 4, 8]))
+    groups = int(rng.integers(1, 9))
+    prefix = int(rng.integers(1, 1500))
+    suffix_hi = int(rng.choice([0, 20, 300, 900]))
+    bs = int(rng.choice([8, 16, 32]))
+    spec = W.Spec(f"randp{seed}", dtype, gs * groups, g * hkv, hkv, d, "prefix", prefix_len=prefix,
+                  group_size=gs, suffix_lo=0, suffix_hi=suffix_hi, block_size=bs)
+    return spec, int(rng.choice([0, 0, 32, 100000]))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_prefix_decode_matches_oracle(seed):
+    spec, min_prefix = _draw_prefix(2000 + seed)
+    say(f"[random prefix] seed {seed}: {spec.dtype} D={spec.head_dim} Hkv={spec.num_kv_heads} "
+        f"G={spec.num_q_heads // spec.num_kv_heads} groups of {spec.group_size} x {spec.num_seqs // spec.group_size} "
+        f"prefix={spec.prefix_len} suffix<= {spec.suffix_hi} bs={spec.block_size} min_prefix={min_prefix}")
+    w = W.Workload(spec, seed=seed)
+    cache = build_cache(w, DEVICE, fill=float("nan"))
+    seqs = list(range(spec.num_seqs))
+    cache.append_tokens(seqs, w.new_k, w.new_v)
+    # a shuffled batch, with one sequence left out when there are several
+    order = list(np.random.default_rng(seed).permutation(spec.num_seqs))
+    batch = order[:-1] if len(order) > 2 else order
+    bt, ctx, maxc = cache.tables(batch)
+    sp, offs, mem, mx = cache.pool.prefix_groups(batch, min_prefix)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEVICE)
+    q = w.q[batch].to(DEVICE).contiguous()
+    out = torch.empty_like(q)
+    binding.paged_attn_decode_prefix(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale,
+                                     dev(sp), dev(offs), dev(mem), mx)
+    torch.cuda.synchronize()
+    err = max_err(out.cpu(), oracle_out(w, batch))
+    say(f"    groups {len(offs) - 1}, longest shared prefix {mx}: max abs err {err:.3e}")
+    assert torch.isfinite(out.float()).all()
+    assert err <= TOL[spec.dtype], err
