@@ -274,8 +274,9 @@ PKV_API size_t pkv_paged_attn_noalloc_scratch_bytes(void);
  * the whole group: a work-group takes 32 prefix tiles (512 tokens) of one KV head and its
  * waves take the group's query rows (member x query head), so every prefix tile is read once
  * for the group.
- * Each sequence's own remainder is attended by the even split over the GPU, and the two parts
- * are merged exactly with the log-sum-exp rule (fixed order: deterministic).
+ * Each sequence's own remainder is attended by the even split over the GPU, and a third launch
+ * merges the two parts (and the pieces of remainders the split cut) exactly with the
+ * log-sum-exp rule (fixed order: deterministic).
  *
  * Arguments as for pkv_paged_attn_decode (f16/bf16 pools, block size 8, 16 or 32, at most 8192
  * sequences; no partition_size), plus the group description that pkv_pool_prefix_groups
@@ -322,9 +323,10 @@ PKV_API pkv_status pkv_paged_attn_decode_prefix(void* out, const void* q,
 PKV_API int32_t pkv_set_merge_spin_limit(int32_t limit);
 
 /* Bytes of workspace pkv_paged_attn_decode_prefix needs (the even split's, plus fp32
- * suffix results [num_seqs][num_q_heads][head_dim + 1] and prefix partials
- * [num_seqs][num_q_heads][ceil(max_prefix_tokens / 512)][head_dim + 2], each region rounded up
- * to 256 bytes).  0 for arguments the call would reject. */
+ * suffix results [num_seqs][num_q_heads][head_dim + 1], prefix partials
+ * [num_seqs][num_q_heads][ceil(max_prefix_tokens / 512)][head_dim + 2] and num_seqs + 2 int32
+ * of suffix bookkeeping, each region rounded up to 256 bytes).  0 for arguments the call would
+ * reject. */
 PKV_API size_t pkv_paged_attn_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                                     int32_t num_kv_heads, int32_t head_dim,
                                                     int32_t max_context_len,

@@ -609,11 +609,12 @@ inline int32_t prefix_chunks(int32_t max_prefix_tokens) {
   const int32_t tiles = (max_prefix_tokens + 15) / 16;
   return (tiles + sk::kPrefixChunkTiles - 1) / sk::kPrefixChunkTiles;
 }
-// Workspace of the prefix path beyond the even split's: suffix results and lse, prefix partials.
+// Workspace of the prefix path beyond the even split's: suffix results and lse, prefix partials,
+// the suffix tile-list prefix sum and ranges in use.
 size_t prefix_extra_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t chunks) {
   const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads;
   return align256(rows * head_dim * 4) + align256(rows * 4) + align256(rows * chunks * head_dim * 4) +
-         align256(rows * chunks * 8);
+         align256(rows * chunks * 8) + align256((static_cast<size_t>(num_seqs) + 2) * 4);
 }
 
 // Shared body of the decode entry points.  With new_key/new_value set, each sequence's
@@ -714,8 +715,8 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
       if (err != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
       return PKV_OK;
     }
-    // prefix-shared: prefix kernel, even split over the suffixes into fp32 partial results,
-    // then the combine writes out.  (A second stream for the prefix kernel does not pay here:
+    // prefix-shared: prefix kernel, even split over the suffixes into fp32 partial results
+    // (or records, for suffixes its ranges cut), then the finalize kernel writes out.  (A second stream for the prefix kernel does not pay here:
     // its work-groups fill every CU, so the two passes hardly overlap, and the cross-stream
     // wait before the combine costs more than the overlap gains.)
     const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads;
@@ -727,9 +728,12 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
     float* pre_acc = reinterpret_cast<float*>(w);
     w += align256(rows * chunks * D * 4);
     float* pre_ml = reinterpret_cast<float*>(w);
+    w += align256(rows * chunks * 8);
+    int32_t* cu = reinterpret_cast<int32_t*>(w);
     sp.seq_start = pre->seq_prefix;
     sp.part_out = part_out;
     sp.part_lse = part_lse;
+    sp.ws_cu = cu;
     sk::PrefixParams pp{};
     pp.q = q;
     pp.k_cache = k_cache;
@@ -742,6 +746,9 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
     pp.pre_ml = pre_ml;
     pp.part_out = part_out;
     pp.part_lse = part_lse;
+    pp.rec_acc = sp.ws_acc;
+    pp.rec_ml = sp.ws_ml;
+    pp.cu = cu;
     pp.out = out;
     pp.num_seqs = num_seqs;
     pp.num_q_heads = num_q_heads;
@@ -756,7 +763,7 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
     pp.scale_log2e = sp.scale_log2e;
     hipError_t err = pre->num_groups > 0 && chunks > 0 ? sk::prefix_launch(pp, cache->dtype, st) : hipSuccess;
     if (err == hipSuccess) err = sk::sk_launch(sp, cache->dtype, st);
-    if (err == hipSuccess) err = sk::combine_launch(pp, cache->dtype, st);
+    if (err == hipSuccess) err = sk::finalize_launch(pp, cache->dtype, st);
     if (err != hipSuccess) return fail(PKV_ERR_HIP, "prefix decode launch: %s", hipGetErrorString(err));
     return PKV_OK;
   }

@@ -62,10 +62,6 @@ constexpr int kFirst = 1 << 9;            // tile flag: first tile of its sequen
 constexpr int kHalf = 1 << 10;            // tile flag (32-token blocks): second half of its block
 __device__ __forceinline__ int clamp_ctx(int L, int maxc) { return L < 0 ? 0 : (L > maxc ? maxc : L); }
 
-// Range (within one KV head) whose tiles include tile t: the largest r with r*n/R <= t.
-__device__ __forceinline__ int range_of(int t, int n, int R) {
-  return static_cast<int>(((static_cast<int64_t>(t) + 1) * R - 1) / n);
-}
 
 // Writes a wave's G output rows, which are contiguous in memory (row r16 < G holds columns
 // 16c + 4grp .. +3 in v[c]), as 16-byte stores of consecutive lanes.  The rows are staged in
@@ -225,6 +221,11 @@ void decode_sk_kernel(SkParams p) {
   __syncthreads();
   const int ntiles = s_cu[B];
   const int R = min(p.ranges, ntiles);  // ranges in use: none of them is empty
+  if (SUFFIX && blockIdx.x == 0) {
+    // the prefix-shared decode's finalize kernel finds each sequence's ranges from these
+    for (int i = tid; i <= B; i += kThreads) p.ws_cu[i] = s_cu[i];
+    if (tid == 0) p.ws_cu[B + 1] = R;
+  }
   if (blockIdx.x == 0 && tid == 0) p.ws_status[0] = kStatusOk;  // the merge kernel runs after this launch
   if (hg == 0 && tid == 0) {
     // the merge kernel's work list: the sequence cut at this range's start, if this is the
@@ -847,7 +848,7 @@ hipError_t launch(const SkParams& p, hipStream_t stream) {
       hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, false, HEADS, false>), grid, block, lds, stream, p);
   }
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || p.ws_cu) return err;  // suffix mode: the finalize kernel merges
   hipLaunchKernelGGL((merge_sk_kernel<T, D, HEADS>), dim3(p.ranges * hgroups), dim3(kMergeThreads),
                      static_cast<size_t>(merge_lds_bytes(D, HEADS)), stream, p);
   return hipGetLastError();

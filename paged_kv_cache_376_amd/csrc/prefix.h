@@ -11,8 +11,8 @@ namespace sk {
 
 // Prefix-shared decode: the tokens a group of sequences shares at the start of its contexts
 // (the same physical blocks) are attended once per group by the prefix kernel, the rest of
-// each context by the even split in suffix and partial-result mode, and a combine kernel merges
-// the two.
+// each context by the even split in suffix and partial-result mode, and a finalize kernel merges
+// the two (with the records of suffixes the split cut).
 constexpr int kPrefixChunkTiles = 32;  // 16-token tiles per prefix work-group (512 tokens)
 
 struct PrefixParams {
@@ -26,7 +26,10 @@ struct PrefixParams {
   float* pre_acc;                // [B][Hq][chunks][D] unnormalised prefix partials
   float* pre_ml;                 // [B][Hq][chunks][2] (running max, sum)
   const float* part_out;         // suffix results of the even split (normalised fp32) ...
-  const float* part_lse;         // ... and their log2-sum-exp
+  const float* part_lse;         // ... and their log2-sum-exp, for suffixes inside one range
+  const float* rec_acc;          // the even split's records (suffixes cut by its ranges):
+  const float* rec_ml;           //   acc [ranges][Hkv][2][16][D], (m, l) [ranges][Hkv][2][16][2]
+  const int32_t* cu;             // [B + 2] its tile-list prefix sum and ranges in use
   void* out;
   int32_t num_seqs;
   int32_t num_q_heads;
@@ -43,8 +46,8 @@ struct PrefixParams {
 
 // Enqueues the prefix kernel (grid num_groups * chunks * Hkv).
 hipError_t prefix_launch(const PrefixParams& pp, int32_t dtype, hipStream_t stream);
-// Enqueues the combine kernel (prefix partials + suffix results -> out).
-hipError_t combine_launch(const PrefixParams& pp, int32_t dtype, hipStream_t stream);
+// Enqueues the finalize kernel (suffix results or records + prefix partials -> out).
+hipError_t finalize_launch(const PrefixParams& pp, int32_t dtype, hipStream_t stream);
 
 }  // namespace sk
 }  // namespace pkv

@@ -60,6 +60,10 @@ struct SkParams {
   // scale*log2(e)*logit; -inf for an empty context), instead of to out.
   float* part_out;
   float* part_lse;
+  // Suffix mode: [B + 2] the tile-list prefix sum (B + 1 entries) and the ranges in use, written
+  // by the first work-group for the finalize kernel; when set, the merge kernel is not launched
+  // (the finalize kernel folds the records of cut suffixes).
+  int32_t* ws_cu;
 };
 
 // KV heads per work-group of the even split for a batch of num_seqs sequences: 4, or 1 below

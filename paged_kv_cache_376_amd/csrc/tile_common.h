@@ -114,6 +114,12 @@ __device__ __forceinline__ void store4(typename T::raw* dst, f32x4 v) {
                               reinterpret_cast<unsigned long long*>(dst));
 }
 
+// Range (within one KV head's list of n tiles cut into R equal ranges) whose tiles include
+// tile t: the largest r with r*n/R <= t.
+__device__ __forceinline__ int range_of(int t, int n, int R) {
+  return static_cast<int>(((static_cast<int64_t>(t) + 1) * R - 1) / n);
+}
+
 // LDS row pitch of a K/V tile: the transposing V reads of one MFMA hit distinct banks.
 __host__ __device__ constexpr int sk_pitch(int D) { return D == 128 ? 288 : 160; }
 

@@ -401,16 +401,17 @@ def test_even_split_is_taken_only_where_its_lds_fits(g, d):
 
 def test_prefix_workspace_size():
     """The prefix-shared decode's workspace: the even split's (rounded up to 256 bytes), then
-    fp32 suffix results [B][Hq][D], their log-sum-exp [B][Hq], and prefix partials (acc
-    [B][Hq][chunks][D] and (m, l) [B][Hq][chunks][2]) with one chunk per 512 prefix tokens,
-    each region rounded up to 256 bytes."""
+    fp32 suffix results [B][Hq][D], their log-sum-exp [B][Hq], prefix partials (acc
+    [B][Hq][chunks][D] and (m, l) [B][Hq][chunks][2]) with one chunk per 512 prefix tokens, and
+    B + 2 int32 of suffix bookkeeping, each region rounded up to 256 bytes."""
     up = lambda x: -(-x // 256) * 256
     for (b, hq, hkv, d, maxc, pre) in [(128, 64, 8, 128, 1537, 1024), (9, 32, 2, 64, 390, 288),
                                        (32, 8, 8, 64, 700, 496), (5, 16, 2, 128, 100, 0)]:
         base = B.paged_attn_workspace_bytes(b, hq, hkv, d, maxc, 0, "bfloat16")
         chunks = -(-(pre // 16) // 32)
         rows = b * hq
-        expect = up(base) + up(rows * d * 4) + up(rows * 4) + up(rows * chunks * d * 4) + up(rows * chunks * 8)
+        expect = (up(base) + up(rows * d * 4) + up(rows * 4) + up(rows * chunks * d * 4) + up(rows * chunks * 8)
+                  + up((b + 2) * 4))
         assert B.paged_attn_decode_prefix_workspace_bytes(b, hq, hkv, d, maxc, pre, "bfloat16") == expect
     # rejected arguments: f32 pools, prefix not a multiple of 16 or longer than the context
     assert B.paged_attn_decode_prefix_workspace_bytes(8, 8, 8, 64, 100, 32, "float32") == 0
