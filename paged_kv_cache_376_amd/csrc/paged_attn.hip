@@ -715,8 +715,9 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
       if (err != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
       return PKV_OK;
     }
-    // prefix-shared: prefix kernel, even split over the suffixes into fp32 partial results
-    // (or records, for suffixes its ranges cut), then the finalize kernel writes out.  (A second stream for the prefix kernel does not pay here:
+    // prefix-shared: the prefix pass and the even split over the suffixes in one launch (fp32
+    // partials, suffix results, records of suffixes its ranges cut), then the finalize kernel
+    // writes out.  (A second stream for the prefix kernel does not pay here:
     // its work-groups fill every CU, so the two passes hardly overlap, and the cross-stream
     // wait before the combine costs more than the overlap gains.)
     const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads;
@@ -761,8 +762,8 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
     pp.num_groups = pre->num_groups;
     pp.chunks = chunks;
     pp.scale_log2e = sp.scale_log2e;
-    hipError_t err = pre->num_groups > 0 && chunks > 0 ? sk::prefix_launch(pp, cache->dtype, st) : hipSuccess;
-    if (err == hipSuccess) err = sk::sk_launch(sp, cache->dtype, st);
+    hipError_t err = pre->num_groups > 0 && chunks > 0 ? sk::sk_launch_prefix(sp, pp, cache->dtype, st)
+                                                       : sk::sk_launch(sp, cache->dtype, st);
     if (err == hipSuccess) err = sk::finalize_launch(pp, cache->dtype, st);
     if (err != hipSuccess) return fail(PKV_ERR_HIP, "prefix decode launch: %s", hipGetErrorString(err));
     return PKV_OK;

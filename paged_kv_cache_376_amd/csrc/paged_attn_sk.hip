@@ -44,6 +44,7 @@
 
 #include "dtypes.h"
 #include "pkv_internal.h"
+#include "prefix_body.h"
 #include "stream_k.h"
 #include "tile_common.h"
 
@@ -158,9 +159,9 @@ __host__ __device__ inline int sk_lds_bytes(int B, int D, int G) {
 // accumulates weight x its V columns; the weights stay fp32.  At a sequence's end the 16 token
 // lanes of each lane row are summed and the columns moved (through the wave's LDS tile) to the
 // layout of the matrix path, which the rest of the kernel shares.
+// The body of one work-group (index bid) of the decode launch, with s_dyn its dynamic LDS.
 template <typename T, int D, int BS, bool SUFFIX, int HEADS, bool VEC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_sk_kernel(SkParams p) {
+__device__ __forceinline__ void decode_sk_body(const SkParams& p, int bid, unsigned char* s_dyn) {
   constexpr int kHeads = HEADS, kSplits = kWaves / HEADS;
   using M = Mma<T>;
   using raw = typename T::raw;
@@ -177,14 +178,13 @@ void decode_sk_kernel(SkParams p) {
   // are dispatched together
   const int hw = wave % kHeads, sw = wave / kHeads;
   const int hgroups = (p.num_kv_heads + kHeads - 1) / kHeads;
-  const int hg = blockIdx.x % hgroups;
-  const int wgr = blockIdx.x / hgroups;
+  const int hg = bid % hgroups;
+  const int wgr = bid / hgroups;
   const int g = hg * kHeads + hw;
   const bool head_ok = g < p.num_kv_heads;
   const int G = p.group;
   const int B = p.num_seqs;
 
-  extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
   int* s_cu = reinterpret_cast<int*>(s_dyn);                  // [B + 1]
   int* s_start = s_cu + ((B + 1 + 3) & ~3);                    // [B] tokens skipped per sequence
   unsigned char* s_work = s_dyn + sk_cu_bytes(B);              // V tiles, later wave states
@@ -221,12 +221,12 @@ void decode_sk_kernel(SkParams p) {
   __syncthreads();
   const int ntiles = s_cu[B];
   const int R = min(p.ranges, ntiles);  // ranges in use: none of them is empty
-  if (SUFFIX && blockIdx.x == 0) {
+  if (SUFFIX && bid == 0) {
     // the prefix-shared decode's finalize kernel finds each sequence's ranges from these
     for (int i = tid; i <= B; i += kThreads) p.ws_cu[i] = s_cu[i];
     if (tid == 0) p.ws_cu[B + 1] = R;
   }
-  if (blockIdx.x == 0 && tid == 0) p.ws_status[0] = kStatusOk;  // the merge kernel runs after this launch
+  if (bid == 0 && tid == 0) p.ws_status[0] = kStatusOk;  // the merge kernel runs after this launch
   if (hg == 0 && tid == 0) {
     // the merge kernel's work list: the sequence cut at this range's start, if this is the
     // first range boundary inside it, with the ranges that hold its first and last tiles
@@ -613,6 +613,30 @@ void decode_sk_kernel(SkParams p) {
   if (open) record(before ? 0 : 1);
 }
 
+template <typename T, int D, int BS, bool SUFFIX, int HEADS, bool VEC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_sk_kernel(SkParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
+  decode_sk_body<T, D, BS, SUFFIX, HEADS, VEC>(p, blockIdx.x, s_dyn);
+}
+
+// The prefix-shared decode's prefix pass and suffix pass in one launch: each work-group first
+// takes its units of the prefix pass (units blockIdx.x, + gridDim.x, ...), then its range of the
+// even split over the suffixes.  Both passes fill the GPU; running them back to back inside
+// each work-group saves a launch boundary, and work-groups that finish their prefix units early
+// start streaming suffix tiles while the others still read prefix tiles.
+template <typename T, int D, int BS, int HEADS, bool VEC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void prefix_suffix_kernel(SkParams p, PrefixParams pp) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
+  const int units = pp.num_groups * pp.chunks * pp.num_kv_heads;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    prefix_unit<T, D, BS>(pp, u, s_dyn);
+    __syncthreads();  // the next unit, or the even split, reuses the LDS
+  }
+  decode_sk_body<T, D, BS, true, HEADS, VEC>(p, blockIdx.x, s_dyn);
+}
+
 // Merge of the sequences cut by range boundaries, and the pool writes of a fused append.
 //
 // One work-group of 8 waves per (range r, group of 4 KV heads).  The range's descriptor names
@@ -854,6 +878,31 @@ hipError_t launch(const SkParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename T, int D, int BS, int HEADS>
+hipError_t launch_prefix(const SkParams& p, const PrefixParams& pp, hipStream_t stream) {
+  const int sk_lds = sk_lds_bytes(p.num_seqs, D, p.group), pre_lds = prefix_tile_lds_bytes(D);
+  const size_t lds = static_cast<size_t>(sk_lds > pre_lds ? sk_lds : pre_lds);
+  const int hgroups = (p.num_kv_heads + HEADS - 1) / HEADS;
+  const dim3 grid(p.ranges * hgroups), block(kThreads);
+  if (p.group == 1)
+    hipLaunchKernelGGL((prefix_suffix_kernel<T, D, BS, HEADS, true>), grid, block, lds, stream, p, pp);
+  else
+    hipLaunchKernelGGL((prefix_suffix_kernel<T, D, BS, HEADS, false>), grid, block, lds, stream, p, pp);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int BS>
+hipError_t launch_prefix_heads(const SkParams& p, const PrefixParams& pp, hipStream_t stream) {
+  return sk_heads(p.num_seqs) == 1 ? launch_prefix<T, D, BS, 1>(p, pp, stream) : launch_prefix<T, D, BS, 4>(p, pp, stream);
+}
+
+template <typename T, int D>
+hipError_t launch_prefix_bs(const SkParams& p, const PrefixParams& pp, hipStream_t stream) {
+  if (p.block_size == 8) return launch_prefix_heads<T, D, 8>(p, pp, stream);
+  if (p.block_size == 32) return launch_prefix_heads<T, D, 32>(p, pp, stream);
+  return launch_prefix_heads<T, D, 16>(p, pp, stream);
+}
+
 template <typename T, int D, int BS>
 hipError_t launch_heads(const SkParams& p, hipStream_t stream) {
   return sk_heads(p.num_seqs) == 1 ? launch<T, D, BS, 1>(p, stream) : launch<T, D, BS, 4>(p, stream);
@@ -903,6 +952,12 @@ size_t sk_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_d
   const size_t ml = static_cast<size_t>(recs) * 32 * sizeof(float);
   const size_t desc = static_cast<size_t>(R) * 4 * sizeof(int32_t);
   return kStatusBytes + acc + ml + desc;
+}
+
+hipError_t sk_launch_prefix(SkParams p, const PrefixParams& pp, int32_t dtype, hipStream_t stream) {
+  const int D = p.head_dim;
+  if (dtype == PKV_BF16) return D == 64 ? launch_prefix_bs<BF16, 64>(p, pp, stream) : launch_prefix_bs<BF16, 128>(p, pp, stream);
+  return D == 64 ? launch_prefix_bs<F16, 64>(p, pp, stream) : launch_prefix_bs<F16, 128>(p, pp, stream);
 }
 
 hipError_t sk_launch(SkParams p, int32_t dtype, hipStream_t stream) {

@@ -44,8 +44,6 @@ struct PrefixParams {
   float scale_log2e;
 };
 
-// Enqueues the prefix kernel (grid num_groups * chunks * Hkv).
-hipError_t prefix_launch(const PrefixParams& pp, int32_t dtype, hipStream_t stream);
 // Enqueues the finalize kernel (suffix results or records + prefix partials -> out).
 hipError_t finalize_launch(const PrefixParams& pp, int32_t dtype, hipStream_t stream);
 

@@ -81,8 +81,12 @@ int sk_lds_bytes_host(int32_t num_seqs, int32_t head_dim, int32_t group);
 bool sk_fits(int32_t num_seqs, int32_t head_dim, int32_t group);
 // Workspace bytes the path needs (host).
 size_t sk_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len);
-// Enqueues the decode kernel and the merge kernel on `stream`.
+// Enqueues the decode kernel and the merge kernel on `stream` (the decode kernel alone in suffix
+// mode, where the prefix-shared decode's finalize kernel merges).
 hipError_t sk_launch(SkParams p, int32_t dtype, hipStream_t stream);
+struct PrefixParams;
+// Enqueues the prefix-shared decode's prefix pass and suffix pass as one launch (suffix mode).
+hipError_t sk_launch_prefix(SkParams p, const PrefixParams& pp, int32_t dtype, hipStream_t stream);
 
 }  // namespace sk
 }  // namespace pkv
