@@ -7,8 +7,9 @@
 // tokens, so it splits exactly into the shared prefix and each sequence's own suffix, merged
 // with the log-sum-exp rule.  The prefix pass reads each prefix tile once for the whole group:
 // a unit of work is one KV head and up to 32 tiles of one group's prefix.  In steps of 8 tiles,
-// each of the work-group's 8 waves loads one tile (K and V) into LDS, and then every wave runs
-// its 16 query rows (member x query head of that KV head) over the step's 8 tiles.  The LDS
+// each of the work-group's 8 waves loads one tile (K and V) into LDS, and then the waves run
+// their 16 query rows (member x query head of that KV head) over the step's 8 tiles (several
+// waves per row tile, each taking part of the tiles, when the group has 64 rows or fewer).  The LDS
 // tiles are double-buffered (144 KiB at D 128): the next step's loads are in flight while the
 // current step is computed, so one barrier per step orders the reuse.  A group with more than
 // 128 rows repeats the pass for each further 128 rows.  (8 waves and 32-tile chunks measured
@@ -33,7 +34,6 @@ constexpr int kPrefixWaves = 8;  // waves per work-group = tiles per step
 template <typename T, int D, int BS>
 __device__ __forceinline__ void prefix_unit(const PrefixParams& pp, int unit, unsigned char* s_t) {
   constexpr int kPrefixStep = kPrefixWaves;
-  constexpr int kRowBlock = 16 * kPrefixWaves;  // query rows per pass
   using M = Mma<T>;
   using raw = typename T::raw;
   constexpr int ROW = D * 2;
@@ -128,10 +128,18 @@ __device__ __forceinline__ void prefix_unit(const PrefixParams& pp, int unit, un
     for (int cc = 0; cc < KC; ++cc) *reinterpret_cast<u32x4*>(kt + TILE_LDS + lds_slot + cc * 64) = vbuf[cc];
   };
 
-  for (int rb = 0; rb * kRowBlock < rows; ++rb) {
+  // With four row tiles or fewer, S waves share a row tile and split each step's tiles between
+  // them (tile t goes to part t % S); their partial results are merged at the end of the unit.
+  // Every wave then computes, instead of only one per row tile, which halves (or better) the
+  // chain of products and exponentials each wave runs per step.
+  const int row_tiles = (rows + 15) / 16;
+  const int S = row_tiles <= 1 ? 8 : row_tiles <= 2 ? 4 : row_tiles <= 4 ? 2 : 1;
+  const int RTc = kPrefixWaves / S;  // row tiles per pass
+  const int my_rt = wave % RTc, part = wave / RTc;
+  for (int rb = 0; rb * 16 * RTc < rows; ++rb) {
     if (rb > 0) __syncthreads();  // the previous pass's last step is read from buffer 0 or 1
     // row r16 of this wave's row tile: member r / G, query head g * G + r % G
-    const int rt0 = rb * kRowBlock + wave * 16;
+    const int rt0 = (rb * RTc + my_rt) * 16;
     const bool has_rows = rt0 < rows;  // wave-uniform
     const int r = rt0 + r16;
     int seq = pp.group_members[mo + (r < rows ? r / G : 0)];
@@ -154,7 +162,7 @@ __device__ __forceinline__ void prefix_unit(const PrefixParams& pp, int unit, un
       issue((j + 1) * kPrefixStep + wave);
       if (!has_rows) continue;
       const int nt = min(kPrefixStep, nk - j * kPrefixStep);
-      for (int t = 0; t < nt; ++t) {
+      for (int t = part; t < nt; t += S) {
         // every prefix tile is full (16 tokens): no masking
         const unsigned char* kt = s_t + ((j & 1) * kPrefixStep + t) * 2 * TILE_LDS;
         const unsigned char* vt = kt + TILE_LDS;
@@ -192,6 +200,32 @@ __device__ __forceinline__ void prefix_unit(const PrefixParams& pp, int unit, un
           acc[cc] = M::pv(vb, pbits, acc[cc]);
         }
       }
+    }
+    if (S > 1) {
+      // parts 1..S-1 leave (m, l, acc) in LDS slot (part - 1) * RTc + my_rt, lane-major
+      // (the tile buffers are free once every wave has passed this barrier); part 0 folds them
+      constexpr int SLOT = 64 * (NC * 16 + 16);
+      __syncthreads();
+      if (has_rows && part > 0) {
+        unsigned char* sl = s_t + ((part - 1) * RTc + my_rt) * SLOT;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) *reinterpret_cast<f32x4*>(sl + (cc * 64 + lane) * 16) = acc[cc];
+        *reinterpret_cast<f32x4*>(sl + (NC * 64 + lane) * 16) = f32x4{m_run, l_run, 0.f, 0.f};
+      }
+      __syncthreads();
+      if (has_rows && part == 0) {
+        for (int q = 1; q < S; ++q) {
+          const unsigned char* sl = s_t + ((q - 1) * RTc + my_rt) * SLOT;
+          const f32x4 ml = *reinterpret_cast<const f32x4*>(sl + (NC * 64 + lane) * 16);
+          const float mn = fmaxf(m_run, ml[0]);
+          const float a0 = __builtin_amdgcn_exp2f(m_run - mn), a1 = __builtin_amdgcn_exp2f(ml[0] - mn);
+          l_run = l_run * a0 + ml[1] * a1;
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc) acc[cc] = acc[cc] * a0 + *reinterpret_cast<const f32x4*>(sl + (cc * 64 + lane) * 16) * a1;
+          m_run = mn;
+        }
+      }
+      if (part > 0) continue;  // uniform: one pass when S > 1
     }
     const float lsum = swap32_sum(swap16_sum(l_run));
     if (valid) {

@@ -52,6 +52,13 @@ CASES = [
     # group of 3 with G = 16 (48 rows), D 64
     ("g16", W.Spec("g16-prefix", "float16", 9, 32, 2, 64, "prefix", prefix_len=300, group_size=3,
                    suffix_lo=0, suffix_hi=90)),
+    # groups of 20 with G = 8: 160 rows per KV head, more than one pass of 8 row tiles
+    ("big-group", W.SPECS["prefix_bf16"].replace(num_seqs=40, group_size=20, prefix_len=600, suffix_hi=120)),
+    # pairs with G = 1: 2 rows per KV head, every wave of the prefix pass on the one row tile
+    ("pairs-mha", W.Spec("pairs-prefix", "bfloat16", 10, 4, 4, 128, "prefix", prefix_len=700, group_size=2,
+                         suffix_lo=0, suffix_hi=40)),
+    # groups of 3 with G = 8: 24 rows, two row tiles with four waves each
+    ("rows24", W.SPECS["prefix_bf16"].replace(num_seqs=12, group_size=3, prefix_len=900, suffix_hi=64)),
     ("bs8", W.SPECS["prefix_bf16"].replace(num_seqs=16, prefix_len=200, suffix_hi=100, block_size=8)),
     ("bs32", W.SPECS["prefix_bf16"].replace(num_seqs=16, prefix_len=200, suffix_hi=100, block_size=32)),
     # a batch under 8 sequences (one KV head per decode work-group) with suffixes long enough
