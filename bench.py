@@ -68,7 +68,7 @@ def prefix_shared_bytes(w, seq_prefix, group_offsets, group_members):
 # decode call of each workload, keyed by (workload, mode), and the kernel sources they were taken on
 _CSRC = os.path.join(ROOT, "paged_kv_cache_376_amd", "csrc")
 SK_SOURCES = [os.path.join(_CSRC, f) for f in ("paged_attn_sk.hip", "tile_common.h", "stream_k.h", "dtypes.h")]
-PREFIX_SOURCES = SK_SOURCES + [os.path.join(_CSRC, f) for f in ("paged_attn_prefix.hip", "prefix.h")]
+PREFIX_SOURCES = SK_SOURCES + [os.path.join(_CSRC, f) for f in ("paged_attn_prefix.hip", "prefix.h", "prefix_body.h")]
 COUNTER_FILES = {
     ("gqa_bf16", "fused"): ("decode_gqa_bf16_B256_counters.md", SK_SOURCES),
     ("mha_fp16", "fused"): ("decode_mha_fp16_B64_counters.md", SK_SOURCES),
@@ -696,8 +696,8 @@ def main():
         "roofline": {
             "kernel": ("pkv_paged_attn_decode_prefix" if args.prefix_shared else
                        "pkv_paged_attn_decode" if args.separate else "pkv_paged_attn_decode_append") +
-                      (" (prefix kernel, decode over the suffixes, merge of sequences cut by the split, "
-                       "combine)" if args.prefix_shared else
+                      (" (prefix pass and suffix decode in one launch, then the finalize kernel)"
+                       if args.prefix_shared else
                        f" (fixed partitions of {part} tokens: decode kernel, then a reduce when a "
                        f"sequence spans several)" if part else
                        " (decode kernel + merge of sequences cut by the split)"),

@@ -717,9 +717,7 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
     }
     // prefix-shared: the prefix pass and the even split over the suffixes in one launch (fp32
     // partials, suffix results, records of suffixes its ranges cut), then the finalize kernel
-    // writes out.  (A second stream for the prefix kernel does not pay here:
-    // its work-groups fill every CU, so the two passes hardly overlap, and the cross-stream
-    // wait before the combine costs more than the overlap gains.)
+    // writes out.
     const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads;
     unsigned char* w = static_cast<unsigned char*>(workspace) + align256(sk_bytes);
     float* part_out = reinterpret_cast<float*>(w);

@@ -10,9 +10,10 @@ namespace pkv {
 namespace sk {
 
 // Prefix-shared decode: the tokens a group of sequences shares at the start of its contexts
-// (the same physical blocks) are attended once per group by the prefix kernel, the rest of
-// each context by the even split in suffix and partial-result mode, and a finalize kernel merges
-// the two (with the records of suffixes the split cut).
+// (the same physical blocks) are attended once per group by the prefix pass, the rest of each
+// context by the even split in suffix and partial-result mode (both in one launch: each
+// work-group takes its prefix units first, then its range of the split), and a finalize kernel
+// merges the two (with the records of suffixes the split cut).
 constexpr int kPrefixChunkTiles = 32;  // 16-token tiles per prefix work-group (512 tokens)
 
 struct PrefixParams {
