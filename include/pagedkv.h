@@ -274,8 +274,9 @@ PKV_API size_t pkv_paged_attn_noalloc_scratch_bytes(void);
  * the whole group: a work-group takes 32 prefix tiles (512 tokens) of one KV head and its
  * waves take the group's query rows (member x query head), so every prefix tile is read once
  * for the group.
- * Each sequence's own remainder is attended by the even split over the GPU, and a third launch
- * merges the two parts (and the pieces of remainders the split cut) exactly with the
+ * Each sequence's own remainder is attended by the even split over the GPU, in the same launch
+ * (each work-group takes its prefix tiles first, then its range of the split), and a second
+ * launch merges the two parts (and the pieces of remainders the split cut) exactly with the
  * log-sum-exp rule (fixed order: deterministic).
  *
  * Arguments as for pkv_paged_attn_decode (f16/bf16 pools, block size 8, 16 or 32, at most 8192
