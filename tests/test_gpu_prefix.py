@@ -59,6 +59,9 @@ CASES = [
                          suffix_lo=0, suffix_hi=40)),
     # groups of 3 with G = 8: 24 rows, two row tiles with four waves each
     ("rows24", W.SPECS["prefix_bf16"].replace(num_seqs=12, group_size=3, prefix_len=900, suffix_hi=64)),
+    # 4 groups of 4 sharing 8192 tokens: 16 chunks x 8 KV heads x 4 groups = 512 prefix units,
+    # more than the launch's 256 work-groups, so work-groups take several units each
+    ("units-over-grid", W.SPECS["prefix_bf16"].replace(num_seqs=16, group_size=4, prefix_len=8192, suffix_hi=64)),
     ("bs8", W.SPECS["prefix_bf16"].replace(num_seqs=16, prefix_len=200, suffix_hi=100, block_size=8)),
     ("bs32", W.SPECS["prefix_bf16"].replace(num_seqs=16, prefix_len=200, suffix_hi=100, block_size=32)),
     # a batch under 8 sequences (one KV head per decode work-group) with suffixes long enough
