@@ -241,8 +241,12 @@ __device__ __forceinline__ void prefix_unit(const PrefixParams& pp, int unit, un
   }
 }
 
-// LDS bytes of one work-group's prefix tiles.
+// LDS bytes of one work-group's prefix tiles.  At the end of a unit the same LDS holds the
+// partial results of the waves that share a row tile (at most 7 slots of 64 x (D / 16 + 1) x 16
+// bytes).
 __host__ __device__ constexpr int prefix_tile_lds_bytes(int D) { return 2 * kPrefixWaves * 2 * kTile * sk_pitch(D); }
+static_assert(7 * 64 * (128 / 16 + 1) * 16 <= prefix_tile_lds_bytes(128), "prefix merge slots, D 128");
+static_assert(7 * 64 * (64 / 16 + 1) * 16 <= prefix_tile_lds_bytes(64), "prefix merge slots, D 64");
 
 }  // namespace
 }  // namespace sk
