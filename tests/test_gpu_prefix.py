@@ -62,6 +62,9 @@ CASES = [
     # 4 groups of 4 sharing 8192 tokens: 16 chunks x 8 KV heads x 4 groups = 512 prefix units,
     # more than the launch's 256 work-groups, so work-groups take several units each
     ("units-over-grid", W.SPECS["prefix_bf16"].replace(num_seqs=16, group_size=4, prefix_len=8192, suffix_hi=64)),
+    # 2624 sequences in 328 groups of 8 with short prefixes: 2624 prefix units for 256
+    # work-groups, and a prefix sum of tile counts that takes about 21 KB of LDS
+    ("many-groups", W.SPECS["prefix_bf16"].replace(num_seqs=2624, prefix_len=64, suffix_hi=32)),
     ("bs8", W.SPECS["prefix_bf16"].replace(num_seqs=16, prefix_len=200, suffix_hi=100, block_size=8)),
     ("bs32", W.SPECS["prefix_bf16"].replace(num_seqs=16, prefix_len=200, suffix_hi=100, block_size=32)),
     # a batch under 8 sequences (one KV head per decode work-group) with suffixes long enough
