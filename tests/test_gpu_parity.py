@@ -252,6 +252,32 @@ def test_large_groups_with_four_heads_per_work_group(n, g, fused):
             assert torch.equal(cache.v_cache[b, o].cpu().view(torch.int16), w.new_v[s].view(torch.int16))
 
 
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("dtype,hkv,d", [("float16", 13, 64), ("bfloat16", 16, 128), ("float16", 18, 128),
+                                         ("bfloat16", 32, 64)])
+def test_one_head_per_kv_head_with_many_head_groups(dtype, hkv, d, fused):
+    """G = 1 with 13 to 32 KV heads and 12 sequences: the vector path's work-groups take two
+    pairs of heads from the two halves of the head range, including head counts that are not a
+    multiple of 4 (the last group's missing heads idle).  Every output against the oracle; the
+    fused call's appended rows in their slots bit for bit."""
+    n = 12
+    lens = tuple(int(x) for x in np.random.default_rng(70 + hkv).integers(1, 2500, size=n))
+    say(f"[parity G=1 head pairs] {dtype} Hkv={hkv} D={d} fused={fused} lens={lens}")
+    w = W.Workload(W.Spec("mha-pairs", dtype, n, hkv, hkv, d, "fixed", fixed_lengths=lens), seed=71 + hkv)
+    if fused:
+        out, cache, _, _, _, slots = decode_step_fused(w)
+    else:
+        out, *_ = decode_step(w)
+    err = max_err(out, oracle_out(w))
+    say(f"    max abs err {err:.3e}")
+    assert torch.isfinite(out.float()).all() and err <= TOL[dtype], err
+    if fused:
+        for s in range(n):
+            b, o = int(slots[s]) // 16, int(slots[s]) % 16
+            assert torch.equal(cache.k_cache[b, o].cpu().view(torch.int16), w.new_k[s].view(torch.int16))
+            assert torch.equal(cache.v_cache[b, o].cpu().view(torch.int16), w.new_v[s].view(torch.int16))
+
+
 @pytest.mark.parametrize("n", [3807, 4000])
 def test_group_16_at_batches_around_the_lds_limit(n):
     """Group 16 at head_dim 128: up to 3807 sequences the even split's prefix sum and wave
