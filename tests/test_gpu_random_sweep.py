@@ -21,11 +21,11 @@ from tests.gpu_common import DEVICE, TOL, decode_step, decode_step_fused, max_er
 pytestmark = pytest.mark.gpu
 
 
-def _draw(seed):
+def _draw(seed, hkv_choices=(1, 2, 3, 4, 5, 8)):
     rng = np.random.default_rng(seed)
     dtype = rng.choice(["bfloat16", "float16", "float32"], p=[0.5, 0.35, 0.15])
     d = int(rng.choice([64, 128]))
-    hkv = int(rng.choice([1, 2, 3, 4, 5, 8]))
+    hkv = int(rng.choice(hkv_choices))
     g = int(rng.choice([1, 2])) if dtype == "float32" else int(rng.choice([1, 1, 2, 3, 4, 5, 7, 8, 8, 9, 12, 16]))
     b = int(rng.choice([1, 2, 3, 5, 7, 8, 9, 17, 40, 130, 300]))
     # about 1.5M (token x KV head) pairs at most, so that the oracle stays fast
@@ -47,7 +47,17 @@ def _draw(seed):
 
 @pytest.mark.parametrize("seed", range(48))
 def test_random_decode_matches_oracle(seed):
-    spec, partition, fused = _draw(1000 + seed)
+    _check_decode(seed, *_draw(1000 + seed))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_decode_many_kv_heads(seed):
+    """12 to 32 KV heads: 3 to 8 groups of 4 heads per range (with one query head per KV
+    head, the work-groups take two pairs of heads from the two halves of the head range)."""
+    _check_decode(200 + seed, *_draw(4000 + seed, hkv_choices=(12, 16, 20, 24, 32)))
+
+
+def _check_decode(seed, spec, partition, fused):
     say(f"[random] seed {seed}: {spec.dtype} D={spec.head_dim} Hkv={spec.num_kv_heads} "
         f"G={spec.num_q_heads // spec.num_kv_heads} B={spec.num_seqs} bs={spec.block_size} "
         f"partition={partition} fused={fused} max len={max(spec.fixed_lengths)}")
@@ -68,11 +78,11 @@ def test_random_decode_matches_oracle(seed):
         assert torch.equal(cache.v_cache[sl // bs, sl % bs].cpu().view(view), w.new_v.view(view))
 
 
-def _draw_prefix(seed):
+def _draw_prefix(seed, hkv_choices=(1, 2, 4, 8)):
     rng = np.random.default_rng(seed)
     dtype = str(rng.choice(["bfloat16", "float16"]))
     d = int(rng.choice([64, 128]))
-    hkv = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice(hkv_choices))
     g = int(rng.integers(1, 17))
     gs = int(rng.choice([2, 3, 4, 8]))
     groups = int(rng.integers(1, 9))
@@ -86,7 +96,16 @@ def _draw_prefix(seed):
 
 @pytest.mark.parametrize("seed", range(16))
 def test_random_prefix_decode_matches_oracle(seed):
-    spec, min_prefix = _draw_prefix(2000 + seed)
+    _check_prefix(seed, *_draw_prefix(2000 + seed))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_prefix_decode_partial_head_groups(seed):
+    """KV head counts that leave the last group of 4 heads of a work-group partly empty."""
+    _check_prefix(100 + seed, *_draw_prefix(3000 + seed, hkv_choices=(3, 5, 6, 7)))
+
+
+def _check_prefix(seed, spec, min_prefix):
     say(f"[random prefix] seed {seed}: {spec.dtype} D={spec.head_dim} Hkv={spec.num_kv_heads} "
         f"G={spec.num_q_heads // spec.num_kv_heads} groups of {spec.group_size} x {spec.num_seqs // spec.group_size} "
         f"prefix={spec.prefix_len} suffix<= {spec.suffix_hi} bs={spec.block_size} min_prefix={min_prefix}")
