@@ -13,7 +13,7 @@ import oracle
 from paged_kv_cache_376_amd import binding
 from paged_kv_cache_376_amd import workloads as W
 from paged_kv_cache_376_amd.cache import PagedKVCache, build_cache
-from tests.gpu_common import DEVICE, TOL, bits, decode, max_err, oracle_full, oracle_out, say
+from tests.gpu_common import DEVICE, TOL, bits, decode, max_err, oracle_full, oracle_out, rounding_bound, say
 
 pytestmark = pytest.mark.gpu
 
@@ -110,8 +110,10 @@ def test_prefix_decode_mixed_batch_and_no_groups():
 
 
 def test_prefix_decode_deterministic_and_equal_members_equal():
-    """Two runs give the same bits; members with equal suffix content and equal queries give
-    the same bits (the prefix pass treats every row of a group alike)."""
+    """Two runs give the same bits; when every member asks the same question over equal
+    content, every row of a prefix-pass wave is alike (so are its rescale decisions) and the
+    members give the same bits.  Equal members beside different neighbours are bounded by the
+    rounding of the arithmetic instead (next test)."""
     say("[prefix decode] determinism")
     spec = W.SPECS["prefix_bf16"].replace(num_seqs=8, suffix_lo=0, suffix_hi=0, prefix_len=512)
     w = W.Workload(spec, seed=44)
@@ -124,6 +126,57 @@ def test_prefix_decode_deterministic_and_equal_members_equal():
     assert max_err(out, oracle_out(w)) <= TOL["bfloat16"]
     for s in range(1, 8):
         assert torch.equal(bits(out[s]), bits(out[0])), s
+
+
+@pytest.mark.parametrize("dtype", ["bfloat16", "float16"])
+def test_prefix_decode_equal_members_within_the_rounding_bound(dtype):
+    """The prefix-sharing invariant on the prefix-shared decode, where the arithmetic of two
+    equal members can differ: a group of 8 shares a 1024-token prefix, and members 2 and 7 have
+    the same query and the same 300-token suffix content (in blocks of their own) while the
+    others differ.  The prefix pass takes a lazy-rescale decision per wave, and a wave's 16
+    rows are 2 members x 8 query heads (members 2 and 7 sit beside different neighbours), and the
+    suffix split cuts the two suffixes at different places.  Each of the two lies within the
+    rounding bound of the exact result (rounding_bound over its whole context), and the two
+    within twice it."""
+    say(f"[prefix decode] equal members, {dtype}")
+    tdt = getattr(torch, dtype)
+    hq, hkv, d, P, Ls = 64, 8, 128, 1024, 300
+    rng = np.random.default_rng(23)
+    rand = lambda n: torch.from_numpy(rng.standard_normal((n, hkv, d), dtype=np.float32)).to(tdt)
+    kp, vp, ks, vs = rand(P), rand(P), rand(Ls), rand(Ls)
+    lens = {m: (Ls if m in (2, 7) else int(rng.integers(1, 600))) for m in range(1, 9)}
+    nb = P // 16 + sum(-(-n // 16) for n in lens.values()) + 8
+    cache = PagedKVCache(nb, hkv, d, tdt, DEVICE, free_order=rng.permutation(nb), fill=float("nan"))
+    cache.add_sequence(0, kp, vp)
+    suffix = {}
+    for m in range(1, 9):
+        cache.fork(0, m)
+        suffix[m] = (ks, vs) if m in (2, 7) else (rand(lens[m]), rand(lens[m]))
+        cache.extend(m, *suffix[m])
+    cache.free(0)
+    seqs = list(range(1, 9))
+    q = torch.from_numpy(rng.standard_normal((8, hq, d), dtype=np.float32)).to(tdt)
+    q[6] = q[1]  # members 2 and 7 (batch positions 1 and 6) ask the same question
+    bt, ctx, maxc = cache.tables(seqs)
+    sp, offs, mem, mx = cache.pool.prefix_groups(seqs, 0)
+    assert len(offs) == 2 and mx == P
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEVICE)
+    qd = q.to(DEVICE).contiguous()
+    out = torch.empty_like(qd)
+    scale = 1.0 / np.sqrt(d)
+    binding.paged_attn_decode_prefix(out, qd, cache.k_cache, cache.v_cache, bt, ctx, maxc, scale,
+                                     dev(sp), dev(offs), dev(mem), mx)
+    torch.cuda.synchronize()
+    out = out.cpu()
+    k = torch.cat([kp, ks])
+    v = torch.cat([vp, vs])
+    ref = oracle.decode_attention(q[1:2], [k], [v], scale)[0]
+    bound = rounding_bound(q[1], k, v, scale, dtype)
+    for i in (1, 6):
+        assert bool((np.abs(out[i].double().numpy() - ref) <= bound).all()), i
+    assert bool((np.abs(out[1].double().numpy() - out[6].double().numpy()) <= 2 * bound).all())
+    say(f"    members 2 and 7: max abs difference {float((out[1].double() - out[6].double()).abs().max()):.3e}, "
+        f"bound up to {bound.max():.3e}")
 
 
 def test_prefix_decode_empty_suffixes():
