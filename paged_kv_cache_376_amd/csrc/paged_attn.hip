@@ -584,7 +584,8 @@ extern "C" size_t pkv_paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
   if (dtype_bytes(dtype) == 0) return 0;
   if (use_stream_k(num_seqs, num_q_heads, num_kv_heads, head_dim, partition_size, dtype))
-    return num_seqs == 0 ? 0 : sk::sk_workspace_bytes(num_seqs, num_kv_heads, head_dim, max_context_len);
+    return num_seqs == 0 ? 0 : sk::sk_workspace_bytes(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim,
+                                                      max_context_len);
   const int32_t part = resolve_partition(max_context_len, partition_size);
   if (part == 0) return 0;
   const int32_t P = parts_for(max_context_len, part);
@@ -677,7 +678,7 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
   if (pre && (!pre->seq_prefix || (pre->num_groups > 0 && (!pre->group_offsets || !pre->group_members))))
     return fail(PKV_ERR_INVALID_ARGUMENT, "NULL group description");
   if (sk_path) {
-    const size_t sk_bytes = sk::sk_workspace_bytes(num_seqs, cache->num_kv_heads, D, max_context_len);
+    const size_t sk_bytes = sk::sk_workspace_bytes(num_seqs, cache->num_kv_heads, G, D, max_context_len);
     const int32_t chunks = pre ? prefix_chunks(pre->max_prefix_tokens) : 0;
     const size_t need = pre ? align256(sk_bytes) + prefix_extra_bytes(num_seqs, num_q_heads, D, chunks) : sk_bytes;
     if (!workspace || workspace_bytes < need)
@@ -701,7 +702,7 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
     sp.max_context_len = max_context_len;
     sp.num_blocks = cache->num_blocks;
     sp.block_size = BS;
-    sp.ranges = sk::sk_ranges(num_seqs, cache->num_kv_heads, max_context_len);
+    sp.ranges = sk::sk_ranges(num_seqs, cache->num_kv_heads, G, max_context_len);
     sp.scale_log2e = scale * kLog2e;
     const int64_t recs = static_cast<int64_t>(sp.ranges) * sp.num_kv_heads * 2;
     sp.ws_status = static_cast<int32_t*>(workspace);
@@ -849,7 +850,7 @@ extern "C" size_t pkv_paged_attn_decode_prefix_workspace_bytes(int32_t num_seqs,
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
   if (max_prefix_tokens < 0 || max_prefix_tokens % 16 != 0 || max_prefix_tokens > max_context_len) return 0;
   if (!use_stream_k(num_seqs, num_q_heads, num_kv_heads, head_dim, 0, dtype)) return 0;
-  return align256(sk::sk_workspace_bytes(num_seqs, num_kv_heads, head_dim, max_context_len)) +
+  return align256(sk::sk_workspace_bytes(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim, max_context_len)) +
          prefix_extra_bytes(num_seqs, num_q_heads, head_dim, prefix_chunks(max_prefix_tokens));
 }
 

@@ -860,21 +860,24 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sk_kernel(SkParams p) {
   }
 }
 
+template <typename T, int D, int BS, int HEADS, bool VEC>
+void launch_decode(const SkParams& p, dim3 grid, size_t lds, hipStream_t stream) {
+  if (p.seq_start)
+    hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, true, HEADS, VEC>), grid, dim3(kThreads), lds, stream, p);
+  else
+    hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, false, HEADS, VEC>), grid, dim3(kThreads), lds, stream, p);
+}
+
 template <typename T, int D, int BS, int HEADS>
 hipError_t launch(const SkParams& p, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(sk_lds_bytes(p.num_seqs, D, p.group));
   const int hgroups = (p.num_kv_heads + HEADS - 1) / HEADS;
-  const dim3 grid(p.ranges * hgroups), block(kThreads);
-  if (p.group == 1) {
-    if (p.seq_start)
-      hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, true, HEADS, true>), grid, block, lds, stream, p);
-    else
-      hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, false, HEADS, true>), grid, block, lds, stream, p);
+  const dim3 grid(p.ranges * hgroups);
+  if constexpr (HEADS == 2) {  // only with a query-head group (sk_heads): no vector-path build
+    launch_decode<T, D, BS, HEADS, false>(p, grid, lds, stream);
   } else {
-    if (p.seq_start)
-      hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, true, HEADS, false>), grid, block, lds, stream, p);
-    else
-      hipLaunchKernelGGL((decode_sk_kernel<T, D, BS, false, HEADS, false>), grid, block, lds, stream, p);
+    if (p.group == 1) launch_decode<T, D, BS, HEADS, true>(p, grid, lds, stream);
+    else launch_decode<T, D, BS, HEADS, false>(p, grid, lds, stream);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.ws_cu) return err;  // suffix mode: the finalize kernel merges
@@ -889,16 +892,22 @@ hipError_t launch_prefix(const SkParams& p, const PrefixParams& pp, hipStream_t 
   const size_t lds = static_cast<size_t>(sk_lds > pre_lds ? sk_lds : pre_lds);
   const int hgroups = (p.num_kv_heads + HEADS - 1) / HEADS;
   const dim3 grid(p.ranges * hgroups), block(kThreads);
-  if (p.group == 1)
-    hipLaunchKernelGGL((prefix_suffix_kernel<T, D, BS, HEADS, true>), grid, block, lds, stream, p, pp);
-  else
+  if constexpr (HEADS == 2) {  // only with a query-head group (sk_heads): no vector-path build
     hipLaunchKernelGGL((prefix_suffix_kernel<T, D, BS, HEADS, false>), grid, block, lds, stream, p, pp);
+  } else {
+    if (p.group == 1)
+      hipLaunchKernelGGL((prefix_suffix_kernel<T, D, BS, HEADS, true>), grid, block, lds, stream, p, pp);
+    else
+      hipLaunchKernelGGL((prefix_suffix_kernel<T, D, BS, HEADS, false>), grid, block, lds, stream, p, pp);
+  }
   return hipGetLastError();
 }
 
 template <typename T, int D, int BS>
 hipError_t launch_prefix_heads(const SkParams& p, const PrefixParams& pp, hipStream_t stream) {
-  return sk_heads(p.num_seqs) == 1 ? launch_prefix<T, D, BS, 1>(p, pp, stream) : launch_prefix<T, D, BS, 4>(p, pp, stream);
+  const int h = sk_heads(p.num_seqs, p.group);
+  return h == 1 ? launch_prefix<T, D, BS, 1>(p, pp, stream)
+                : h == 2 ? launch_prefix<T, D, BS, 2>(p, pp, stream) : launch_prefix<T, D, BS, 4>(p, pp, stream);
 }
 
 template <typename T, int D>
@@ -910,7 +919,8 @@ hipError_t launch_prefix_bs(const SkParams& p, const PrefixParams& pp, hipStream
 
 template <typename T, int D, int BS>
 hipError_t launch_heads(const SkParams& p, hipStream_t stream) {
-  return sk_heads(p.num_seqs) == 1 ? launch<T, D, BS, 1>(p, stream) : launch<T, D, BS, 4>(p, stream);
+  const int h = sk_heads(p.num_seqs, p.group);
+  return h == 1 ? launch<T, D, BS, 1>(p, stream) : h == 2 ? launch<T, D, BS, 2>(p, stream) : launch<T, D, BS, 4>(p, stream);
 }
 
 template <typename T, int D>
@@ -922,14 +932,14 @@ hipError_t launch_bs(const SkParams& p, hipStream_t stream) {
 
 }  // namespace
 
-int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
-  // About 8 waves per CU on a 256-CU part (one work-group of 8 waves per range and group of 4
-  // KV heads), and at least 8 tiles per range (4 per wave) in the worst case: small batches
+int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t group, int32_t max_context_len) {
+  // About 8 waves per CU on a 256-CU part (one work-group of 8 waves per range and group of
+  // sk_heads KV heads), and at least 8 tiles per range (4 per wave) in the worst case: small batches
   // spread over more of the chip (a batch of 4 x 1024 tokens, G 8: 23 us instead of 39 us at
   // 32 tiles per range) without ranges so short that merging their records dominates.
   const int64_t max_blocks = (static_cast<int64_t>(max_context_len) + kTile - 1) / kTile;
   const int64_t upper_tiles = static_cast<int64_t>(num_seqs) * max_blocks;
-  const int64_t heads = sk_heads(num_seqs);
+  const int64_t heads = sk_heads(num_seqs, group);
   const int64_t hgroups = (num_kv_heads + heads - 1) / heads;
   int64_t r = kSkTargetWaves / (hgroups * kWaves);
   if (r < 1) r = 1;
@@ -945,13 +955,14 @@ int sk_lds_bytes_host(int32_t num_seqs, int32_t head_dim, int32_t group) {
 bool sk_fits(int32_t num_seqs, int32_t head_dim, int32_t group) {
   if (num_seqs < 0 || num_seqs > kSkMaxSeqs || group < 1 || group > 16) return false;
   if (head_dim != 64 && head_dim != 128) return false;
-  const int heads = sk_heads(num_seqs);
+  const int heads = sk_heads(num_seqs, group);
   return sk_lds_bytes_host(num_seqs, head_dim, group) <= kLdsPerWorkgroup &&
          merge_lds_bytes(head_dim, heads) + static_cast<int>(kWaves * sizeof(int)) <= kLdsPerWorkgroup;
 }
 
-size_t sk_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len) {
-  const int64_t R = sk_ranges(num_seqs, num_kv_heads, max_context_len);
+size_t sk_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t group, int32_t head_dim,
+                          int32_t max_context_len) {
+  const int64_t R = sk_ranges(num_seqs, num_kv_heads, group, max_context_len);
   const int64_t recs = R * num_kv_heads * 2;
   const size_t acc = static_cast<size_t>(recs) * 16 * head_dim * sizeof(float);
   const size_t ml = static_cast<size_t>(recs) * 32 * sizeof(float);

@@ -66,12 +66,21 @@ struct SkParams {
   int32_t* ws_cu;
 };
 
-// KV heads per work-group of the even split for a batch of num_seqs sequences: 4, or 1 below
-// 8 sequences.  A small batch is cut into many ranges per sequence; one head per work-group
-// with eight sub-ranges merged in LDS leaves the merge kernel a quarter of the records.
-inline int32_t sk_heads(int32_t num_seqs) { return num_seqs < 8 ? 1 : 4; }
+// KV heads per work-group of the even split (group: query heads per KV head).  The launch
+// keeps about 256 work-groups, so the fewer heads a work-group takes, the fewer ranges each
+// head's tile list is cut into, and the fewer records the cut sequences leave:
+//   * 1 below 8 sequences: a small batch is cut into many ranges per sequence; one head with
+//     eight sub-ranges merged in LDS leaves the merge kernel a quarter of the records;
+//   * 2 below 32 sequences when a head serves a query-head group (4 sub-ranges): half the
+//     ranges of 4 heads per work-group.  Measured, same process: 29.8 -> 23.4 us on 16
+//     lognormal 70B-GQA sequences, 192.5 -> 190.1 us on 8 x 32768 tokens; from about 32
+//     uniform long sequences up, the narrower 512-byte row slices cost more than they save;
+//   * 4 otherwise: four adjacent 256-byte slices of each token row, 2 sub-ranges.
+inline int32_t sk_heads(int32_t num_seqs, int32_t group) {
+  return num_seqs < 8 ? 1 : (num_seqs < 32 && group >= 2) ? 2 : 4;
+}
 // Ranges per KV head for these arguments (host).
-int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len);
+int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t group, int32_t max_context_len);
 // LDS bytes of the decode kernel for these shapes (host), dynamic and static together;
 // above 64 KiB needs no opt-in here.
 int sk_lds_bytes_host(int32_t num_seqs, int32_t head_dim, int32_t group);
@@ -80,7 +89,8 @@ int sk_lds_bytes_host(int32_t num_seqs, int32_t head_dim, int32_t group);
 // large batches with large groups do not fit (group 16, head_dim 128: up to 3807 sequences).
 bool sk_fits(int32_t num_seqs, int32_t head_dim, int32_t group);
 // Workspace bytes the path needs (host).
-size_t sk_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len);
+size_t sk_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t group, int32_t head_dim,
+                          int32_t max_context_len);
 // Enqueues the decode kernel and the merge kernel on `stream` (the decode kernel alone in suffix
 // mode, where the prefix-shared decode's finalize kernel merges).
 hipError_t sk_launch(SkParams p, int32_t dtype, hipStream_t stream);

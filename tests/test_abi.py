@@ -348,6 +348,12 @@ def test_workspace_size_and_partition_rules():
     # large ones: about 2048 waves (8 per work-group, 4 KV heads each -> 128 ranges at 8 KV heads)
     assert ws(4, 64, 8, 128, 1024, 0) == status + 32 * per_range128
     assert ws(256, 64, 8, 128, 8192, 0) == status + 128 * per_range128
+    # 8 to 31 sequences with a query-head group: 2 KV heads per work-group, half the ranges
+    # (64 at 8 KV heads); with one query head per KV head, still 4 (32 ranges at 32 KV heads)
+    assert ws(8, 64, 8, 128, 8192, 0) == status + 64 * per_range128
+    assert ws(31, 64, 8, 128, 8192, 0) == status + 64 * per_range128
+    assert ws(32, 64, 8, 128, 8192, 0) == status + 128 * per_range128
+    assert ws(16, 32, 32, 128, 2048, 0) == status + 32 * (2 * 32 * rec128 + 16)
     # tiny contexts: at most one range per 8 worst-case tiles
     assert ws(1, 8, 1, 128, 16, 0) <= status + 2 * rec128 + 256
     assert ws(0, 64, 8, 128, 8192, 0) == 0
