@@ -905,7 +905,7 @@ hipError_t launch_prefix(const SkParams& p, const PrefixParams& pp, hipStream_t 
 
 template <typename T, int D, int BS>
 hipError_t launch_prefix_heads(const SkParams& p, const PrefixParams& pp, hipStream_t stream) {
-  const int h = sk_heads(p.num_seqs, p.group);
+  const int h = sk_heads(p.num_seqs, p.num_kv_heads, p.group);
   return h == 1 ? launch_prefix<T, D, BS, 1>(p, pp, stream)
                 : h == 2 ? launch_prefix<T, D, BS, 2>(p, pp, stream) : launch_prefix<T, D, BS, 4>(p, pp, stream);
 }
@@ -919,7 +919,7 @@ hipError_t launch_prefix_bs(const SkParams& p, const PrefixParams& pp, hipStream
 
 template <typename T, int D, int BS>
 hipError_t launch_heads(const SkParams& p, hipStream_t stream) {
-  const int h = sk_heads(p.num_seqs, p.group);
+  const int h = sk_heads(p.num_seqs, p.num_kv_heads, p.group);
   return h == 1 ? launch<T, D, BS, 1>(p, stream) : h == 2 ? launch<T, D, BS, 2>(p, stream) : launch<T, D, BS, 4>(p, stream);
 }
 
@@ -939,7 +939,7 @@ int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t group, int32_t
   // 32 tiles per range) without ranges so short that merging their records dominates.
   const int64_t max_blocks = (static_cast<int64_t>(max_context_len) + kTile - 1) / kTile;
   const int64_t upper_tiles = static_cast<int64_t>(num_seqs) * max_blocks;
-  const int64_t heads = sk_heads(num_seqs, group);
+  const int64_t heads = sk_heads(num_seqs, num_kv_heads, group);
   const int64_t hgroups = (num_kv_heads + heads - 1) / heads;
   int64_t r = kSkTargetWaves / (hgroups * kWaves);
   if (r < 1) r = 1;
@@ -955,9 +955,11 @@ int sk_lds_bytes_host(int32_t num_seqs, int32_t head_dim, int32_t group) {
 bool sk_fits(int32_t num_seqs, int32_t head_dim, int32_t group) {
   if (num_seqs < 0 || num_seqs > kSkMaxSeqs || group < 1 || group > 16) return false;
   if (head_dim != 64 && head_dim != 128) return false;
-  const int heads = sk_heads(num_seqs, group);
+  // the merge kernel's LDS for the largest need among the head counts sk_heads can choose
+  int merge = 0;
+  for (int heads : {1, 2, 4}) merge = merge > merge_lds_bytes(head_dim, heads) ? merge : merge_lds_bytes(head_dim, heads);
   return sk_lds_bytes_host(num_seqs, head_dim, group) <= kLdsPerWorkgroup &&
-         merge_lds_bytes(head_dim, heads) + static_cast<int>(kWaves * sizeof(int)) <= kLdsPerWorkgroup;
+         merge + static_cast<int>(kWaves * sizeof(int)) <= kLdsPerWorkgroup;
 }
 
 size_t sk_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t group, int32_t head_dim,

@@ -75,9 +75,12 @@ struct SkParams {
 //     ranges of 4 heads per work-group.  Measured, same process: 29.8 -> 23.4 us on 16
 //     lognormal 70B-GQA sequences, 192.5 -> 190.1 us on 8 x 32768 tokens; from about 32
 //     uniform long sequences up, the narrower 512-byte row slices cost more than they save;
+//   * 2 as well with a single KV head (multi-query attention) at any batch: 4 heads per
+//     work-group would leave 6 of its 8 waves without a head (256 x 8 query heads on one KV
+//     head: 43.3 -> 32.1 us; 512 sequences: 71.2 -> 47.6 us);
 //   * 4 otherwise: four adjacent 256-byte slices of each token row, 2 sub-ranges.
-inline int32_t sk_heads(int32_t num_seqs, int32_t group) {
-  return num_seqs < 8 ? 1 : (num_seqs < 32 && group >= 2) ? 2 : 4;
+inline int32_t sk_heads(int32_t num_seqs, int32_t num_kv_heads, int32_t group) {
+  return num_seqs < 8 ? 1 : (group >= 2 && (num_seqs < 32 || num_kv_heads == 1)) ? 2 : 4;
 }
 // Ranges per KV head for these arguments (host).
 int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t group, int32_t max_context_len);

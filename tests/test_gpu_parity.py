@@ -278,6 +278,29 @@ def test_one_head_per_kv_head_with_many_head_groups(dtype, hkv, d, fused):
             assert torch.equal(cache.v_cache[b, o].cpu().view(torch.int16), w.new_v[s].view(torch.int16))
 
 
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("n,g,d", [(40, 8, 128), (300, 16, 64), (33, 4, 128)])
+def test_one_kv_head_two_heads_per_work_group(n, g, d, fused):
+    """Multi-query attention (one KV head) with 32 or more sequences: the even split's
+    work-groups take 2 head columns (one of them idle) x 4 sub-ranges.  Every output against the
+    oracle; the fused call's appended rows in their slots bit for bit."""
+    lens = tuple(int(x) for x in np.random.default_rng(80 + n).integers(0, 3000, size=n))
+    say(f"[parity MQA] n={n} G={g} D={d} fused={fused}")
+    w = W.Workload(W.Spec("mqa", "bfloat16", n, g, 1, d, "fixed", fixed_lengths=lens), seed=81 + n)
+    if fused:
+        out, cache, _, _, _, slots = decode_step_fused(w)
+    else:
+        out, *_ = decode_step(w)
+    err = max_err(out, oracle_out(w))
+    say(f"    max abs err {err:.3e}")
+    assert torch.isfinite(out.float()).all() and err <= TOL["bfloat16"], err
+    if fused:
+        for s in range(n):
+            b, o = int(slots[s]) // 16, int(slots[s]) % 16
+            assert torch.equal(cache.k_cache[b, o].cpu().view(torch.int16), w.new_k[s].view(torch.int16))
+            assert torch.equal(cache.v_cache[b, o].cpu().view(torch.int16), w.new_v[s].view(torch.int16))
+
+
 @pytest.mark.parametrize("n", [3807, 4000])
 def test_group_16_at_batches_around_the_lds_limit(n):
     """Group 16 at head_dim 128: up to 3807 sequences the even split's prefix sum and wave
