@@ -78,9 +78,11 @@ struct SkParams {
 //   * 2 as well with a single KV head (multi-query attention) at any batch: 4 heads per
 //     work-group would leave 6 of its 8 waves without a head (256 x 8 query heads on one KV
 //     head: 43.3 -> 32.1 us; 512 sequences: 71.2 -> 47.6 us);
-//   * 4 otherwise: four adjacent 256-byte slices of each token row, 2 sub-ranges.
+//   * 4 otherwise, and with two KV heads at any batch: four adjacent 256-byte slices of each
+//     token row, 2 sub-ranges.  (With two KV heads, 4 heads per work-group keeps 4 of its
+//     waves busy and was 2-5% faster than 2 heads x 4 sub-ranges at 12 to 256 sequences.)
 inline int32_t sk_heads(int32_t num_seqs, int32_t num_kv_heads, int32_t group) {
-  return num_seqs < 8 ? 1 : (group >= 2 && (num_seqs < 32 || num_kv_heads == 1)) ? 2 : 4;
+  return num_seqs < 8 ? 1 : (group >= 2 && num_kv_heads != 2 && (num_seqs < 32 || num_kv_heads == 1)) ? 2 : 4;
 }
 // Ranges per KV head for these arguments (host).
 int32_t sk_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t group, int32_t max_context_len);
