@@ -354,6 +354,10 @@ def test_workspace_size_and_partition_rules():
     assert ws(31, 64, 8, 128, 8192, 0) == status + 64 * per_range128
     assert ws(32, 64, 8, 128, 8192, 0) == status + 128 * per_range128
     assert ws(16, 32, 32, 128, 2048, 0) == status + 32 * (2 * 32 * rec128 + 16)
+    # 4 KV heads at 16 sequences: 2 heads per work-group, 2 head groups of 128 ranges; 2 KV
+    # heads keep 4 heads per work-group: one head group of 256 ranges
+    assert ws(16, 32, 4, 128, 8192, 0) == status + 128 * (2 * 4 * rec128 + 16)
+    assert ws(16, 16, 2, 128, 8192, 0) == status + 256 * (2 * 2 * rec128 + 16)
     # tiny contexts: at most one range per 8 worst-case tiles
     assert ws(1, 8, 1, 128, 16, 0) <= status + 2 * rec128 + 256
     assert ws(0, 64, 8, 128, 8192, 0) == 0
