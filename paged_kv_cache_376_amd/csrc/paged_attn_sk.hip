@@ -183,9 +183,14 @@ __device__ __forceinline__ void decode_sk_body(const SkParams& p, int bid, unsig
   // With one query head per KV head and many head groups (MHA shapes), the four heads of a
   // work-group are two pairs from the two halves of the head range ({0, 1, 2h, 2h + 1}, ...
   // for h head groups): measured 2% faster on 64 x 32-head fp16 decode than four adjacent
-  // heads.  Otherwise four adjacent heads, one contiguous 4 x D run of each token row.
+  // heads.  Otherwise four adjacent heads, one contiguous 4 x D run of each token row; with two
+  // head groups the second group's heads go to the even work-group indices.  Work-groups are
+  // dealt to the 8 XCDs in turn, so head group = XCD parity: in the plain order the last heads
+  // (the second half of each token row) land on the odd XCDs, and both of those read more
+  // slowly (measured with per-work-group clock stamps); swapped, the two offset each other:
+  // 256 lognormal 70B-GQA sequences 168.6 -> 165.5 us, 512 sequences 312.5 -> 307.6 us.
   const int g = (VEC && kHeads == 4 && hgroups >= 4) ? (hw >> 1) * (2 * hgroups) + hg * 2 + (hw & 1)
-                                                     : hg * kHeads + hw;
+                                                     : (kHeads == 4 && hgroups == 2 ? 1 - hg : hg) * kHeads + hw;
   const bool head_ok = g < p.num_kv_heads;
   const int G = p.group;
   const int B = p.num_seqs;
