@@ -249,8 +249,9 @@ PKV_API pkv_status pkv_paged_attn_decode_append(void* out, const void* q,
  * The status word of pkv_paged_attn_workspace_bytes lives at the start of the array, out of the
  * caller's reach.
  * Errors: as pkv_paged_attn_decode_append; WORKSPACE_TOO_SMALL when the arguments need more
- * workspace than the scratch array holds (every even-split decode fits; only large
- * fixed-partition splits, e.g. f32 pools with long contexts and many sequences, do not), with
+ * workspace than the scratch array holds (every even-split decode with at most 2016 KV heads
+ * fits; more KV heads, and large fixed-partition splits, e.g. f32 pools with long contexts and
+ * many sequences, do not), with
  * the sizes in the message; HIP when the scratch array's address cannot be found on the
  * current device. */
 PKV_API pkv_status pkv_paged_attn_decode_append_noalloc(void* out, const void* q,

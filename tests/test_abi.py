@@ -508,3 +508,29 @@ def test_noalloc_decode_rejects_before_touching_the_device():
                                                     ctypes.c_float(0.1), 0, None) == 1
     assert lib.pkv_paged_attn_decode_append_noalloc(16, 16, 16, 16, 16, 16, ctypes.byref(d), 16, 1, 16, 16, 0, 2,
                                                     ctypes.c_float(0.1), 0, None) == 0
+
+
+def test_noalloc_scratch_holds_every_even_split_up_to_2016_kv_heads():
+    """The scratch array of the allocation-free step holds the workspace of every evenly split
+    decode (partition size 0) with at most 2016 KV heads, whatever the batch, group and context;
+    2017 KV heads at head dim 128 need more.  The records grow with ranges x KV heads, and the
+    ranges shrink as the KV heads grow, so the largest need sits at a few hundred ranges."""
+    lib = B.lib()
+    ws = lib.pkv_paged_attn_workspace_bytes
+    part = lib.pkv_paged_attn_partition_size
+    cap = B.noalloc_scratch_bytes()
+    bf16 = 2
+    ctx = 1 << 20
+
+    def worst(hkv, dims=(64, 128)):
+        need = 0
+        for g in (1, 2, 3, 4, 8, 12, 16):
+            for d in dims:
+                for n in (1, 7, 8, 31, 32, 256, 1000, 8192):
+                    if part(n, hkv * g, hkv, d, ctx, 0, bf16) == 0:
+                        need = max(need, ws(n, hkv * g, hkv, d, ctx, 0, bf16))
+        return need
+
+    for hkv in list(range(1, 70)) + [96, 127, 128, 255, 256, 500, 512, 1000, 1024, 1500, 2000, 2015, 2016]:
+        assert 0 < worst(hkv) <= cap, hkv
+    assert worst(2017, dims=(128,)) > cap
