@@ -73,6 +73,7 @@ COUNTER_FILES = {
     ("gqa_bf16", "fused"): ("decode_gqa_bf16_B256_counters.md", SK_SOURCES),
     ("mha_fp16", "fused"): ("decode_mha_fp16_B64_counters.md", SK_SOURCES),
     ("long_bf16", "fused"): ("decode_long_bf16_B8_counters.md", SK_SOURCES),
+    ("prefix_bf16", "fused"): ("decode_prefix_bf16_B128_counters.md", SK_SOURCES),
     ("prefix_bf16", "prefix"): ("decode_prefix_bf16_B128_shared_counters.md", PREFIX_SOURCES),
 }
 
