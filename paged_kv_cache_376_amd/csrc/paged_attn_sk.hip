@@ -181,16 +181,23 @@ __device__ __forceinline__ void decode_sk_body(const SkParams& p, int bid, unsig
   const int hg = bid % hgroups;
   const int wgr = bid / hgroups;
   // With one query head per KV head and many head groups (MHA shapes), the four heads of a
-  // work-group are two pairs from the two halves of the head range ({0, 1, 2h, 2h + 1}, ...
-  // for h head groups): measured 2% faster on 64 x 32-head fp16 decode than four adjacent
-  // heads.  Otherwise four adjacent heads, one contiguous 4 x D run of each token row; with two
+  // work-group are two pairs from the two halves of the head range: pair hg from the first
+  // half, and from the second half pair hg ^ 1 when the head groups are even in number (else
+  // pair hg), e.g. {0, 1, 2h + 2, 2h + 3}, {2, 3, 2h, 2h + 1}, ... for h head groups.  Pairs
+  // from the two halves were 2% faster on 64 x 32-head fp16 decode than four adjacent heads;
+  // taking the second pair from the other parity, so that each work-group reads one 512-byte
+  // slice at an even and one at an odd multiple of 512 bytes into the token row, was another
+  // 0.1-1.3% on 64-256 sequences of 16 or 32 heads (per-work-group clock stamps had shown the
+  // work-groups on even XCDs, which read only even slices, ending about 10 us after the rest).
+  // Otherwise four adjacent heads, one contiguous 4 x D run of each token row; with two
   // head groups the second group's heads go to the even work-group indices.  Work-groups are
   // dealt to the 8 XCDs in turn, so head group = XCD parity: in the plain order the last heads
   // (the second half of each token row) land on the odd XCDs, and both of those read more
   // slowly (measured with per-work-group clock stamps); swapped, the two offset each other:
   // 256 lognormal 70B-GQA sequences 168.6 -> 165.5 us, 512 sequences 312.5 -> 307.6 us.
-  const int g = (VEC && kHeads == 4 && hgroups >= 4) ? (hw >> 1) * (2 * hgroups) + hg * 2 + (hw & 1)
-                                                     : (kHeads == 4 && hgroups == 2 ? 1 - hg : hg) * kHeads + hw;
+  const int g = (VEC && kHeads == 4 && hgroups >= 4)
+                    ? (hw >> 1) * (2 * hgroups) + ((hgroups % 2 == 0 && (hw >> 1)) ? hg ^ 1 : hg) * 2 + (hw & 1)
+                    : (kHeads == 4 && hgroups == 2 ? 1 - hg : hg) * kHeads + hw;
   const bool head_ok = g < p.num_kv_heads;
   const int G = p.group;
   const int B = p.num_seqs;
