@@ -257,8 +257,10 @@ def test_large_groups_with_four_heads_per_work_group(n, g, fused):
                                          ("bfloat16", 32, 64)])
 def test_one_head_per_kv_head_with_many_head_groups(dtype, hkv, d, fused):
     """G = 1 with 13 to 32 KV heads and 12 sequences: the vector path's work-groups take two
-    pairs of heads from the two halves of the head range, including head counts that are not a
-    multiple of 4 (the last group's missing heads idle).  Every output against the oracle; the
+    pairs of heads from the two halves of the head range, the second pair from the other parity
+    when the head groups are even in number (13, 16 and 32 KV heads: 4, 4 and 8 groups) and the
+    same pair index otherwise (18: 5 groups), including head counts that are not a multiple of 4
+    (the missing heads idle).  Every output against the oracle; the
     fused call's appended rows in their slots bit for bit."""
     n = 12
     lens = tuple(int(x) for x in np.random.default_rng(70 + hkv).integers(1, 2500, size=n))
