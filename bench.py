@@ -406,7 +406,7 @@ def measure_step(w, dev, steps, warmup, partition=0, mode="fused"):
     the decode step of `mode`:
       fused    one pkv_paged_attn_decode_append call (the default step);
       separate pkv_kv_cache_append, then pkv_paged_attn_decode;
-      prefix   pkv_kv_cache_append, then pkv_paged_attn_decode_prefix (groups from the pool).
+      prefix   one pkv_paged_attn_decode_prefix_append call (groups from the pool).
     K steps run back to back between two HIP events on the launch stream (after W warm-up
     steps); a second pass of K steps puts events around every call for the per-call times.  The
     append call is also timed on its own.  Returns the times and the byte counts."""
@@ -465,10 +465,11 @@ def measure_step(w, dev, steps, warmup, partition=0, mode="fused"):
         log(f"prefix groups: {len(offs_) - 1}, longest shared prefix {mx_} tokens")
 
         def prefix_call():
-            binding.paged_attn_decode_prefix(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale, sp_d,
-                                             offs_d, mem_d, mx_, workspace=pws_t, stream=stream)
+            binding.paged_attn_decode_prefix_append(out, q, new_k, new_v, cache.k_cache, cache.v_cache, bt, ctx, maxc,
+                                                    w.scale, sp_d, offs_d, mem_d, mx_, workspace=pws_t,
+                                                    stream=stream)
 
-    calls = {"prefix": lambda: [append_call, prefix_call], "separate": lambda: [append_call, decode_call],
+    calls = {"prefix": lambda: [prefix_call], "separate": lambda: [append_call, decode_call],
              "fused": lambda: [fused_call]}[mode]()
     log(f"{sp.name}: warmup {warmup} steps ({mode}, partition {part or 'even split'}, workspace {ws_bytes} B)")
     for _ in range(warmup):
@@ -499,10 +500,10 @@ def measure_step(w, dev, steps, warmup, partition=0, mode="fused"):
     torch.cuda.synchronize()
     t_calls = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(len(calls))] for i in range(steps)])
     t_dec = t_calls[:, -1]
-    t_app = t_calls[:, 0] if mode != "fused" else None
+    t_app = t_calls[:, 0] if mode == "separate" else None
     # the append alone, back to back (it rewrites the same rows into the same slots)
     append_us = _time_calls(append_call, steps, warmup, stream) * 1e6
-    if mode == "fused":
+    if mode != "separate":
         log(f"{sp.name}: step {ms_step * 1e3:.1f} us: fused append+decode call median {np.median(t_dec) * 1e3:.1f} "
             f"us (p10 {np.percentile(t_dec, 10) * 1e3:.1f}, p90 {np.percentile(t_dec, 90) * 1e3:.1f}); "
             f"append alone {append_us:.1f} us")
@@ -516,7 +517,7 @@ def measure_step(w, dev, steps, warmup, partition=0, mode="fused"):
     if mode == "prefix":
         # the method reads each shared prefix once per group: that is the roofline's byte count
         kv_read, dec_bytes = prefix_shared_bytes(w, *groups[:3])
-    if mode == "fused":
+    if mode != "separate":
         dec_bytes += fused_append_bytes(w)
     del cache, ws
     torch.cuda.synchronize()
@@ -539,7 +540,7 @@ def _config_record(w, m, mode):
                     f"{sp.dtype}, block {sp.block_size}, lengths {sp.lengths}, +1 appended token per sequence",
         "step_calls": {"fused": "pkv_paged_attn_decode_append",
                        "separate": "pkv_kv_cache_append + pkv_paged_attn_decode",
-                       "prefix": "pkv_kv_cache_append + pkv_paged_attn_decode_prefix"}[mode],
+                       "prefix": "pkv_paged_attn_decode_prefix_append (append fused into the decode)"}[mode],
         "step_us": round(m["ms_step"] * 1e3, 2),
         "kv_bytes_per_step": m["kv_bytes"],
         "kv_gbs": round(m["kv_bytes"] / step_s / 1e9, 2),
@@ -605,8 +606,8 @@ def main():
                          "(copy-on-write) GB/s; swap: pkv_swap_blocks device<->pinned host GB/s; "
                          "append: pkv_kv_cache_append of a prefill chunk GB/s")
     ap.add_argument("--prefix-shared", action="store_true",
-                    help="decode with pkv_paged_attn_decode_prefix (groups from pkv_pool_prefix_groups), "
-                         "after a separate append")
+                    help="decode with pkv_paged_attn_decode_prefix_append (groups from "
+                         "pkv_pool_prefix_groups, append fused)")
     ap.add_argument("--block-size", type=int, default=0,
                     help="tokens per pool block (default: the workload's, 16)")
     ap.add_argument("--append-tokens", type=int, default=16384,
@@ -641,7 +642,6 @@ def main():
     m = measure_step(w, dev, args.steps, args.warmup, args.partition, mode)
     ms_step, t_dec, t_app, part = m["ms_step"], m["t_dec"], m["t_app"], m["part"]
     kv_bytes, kv_read, dec_bytes = m["kv_bytes"], m["kv_read"], m["dec_bytes"]
-    two_calls = mode != "fused"
     dec_s = float(t_dec.mean()) / 1e3
     gbs = kv_bytes / (ms_step / 1e3) / 1e9
     achieved = dec_bytes / dec_s / 1e9
@@ -680,7 +680,7 @@ def main():
         "decode_us_median": round(float(np.median(t_dec)) * 1e3, 2),
         "decode_us_p10": round(float(np.percentile(t_dec, 10)) * 1e3, 2),
         "decode_us_p90": round(float(np.percentile(t_dec, 90)) * 1e3, 2),
-        "step_calls": "pkv_kv_cache_append + pkv_paged_attn_decode_prefix" if args.prefix_shared
+        "step_calls": "pkv_paged_attn_decode_prefix_append (append fused into the decode)" if args.prefix_shared
                       else "pkv_kv_cache_append + pkv_paged_attn_decode" if args.separate
                       else "pkv_paged_attn_decode_append (append fused into the decode)",
         "config": {
@@ -695,9 +695,10 @@ def main():
             "pool_blocks": w.num_blocks,
         },
         "roofline": {
-            "kernel": ("pkv_paged_attn_decode_prefix" if args.prefix_shared else
+            "kernel": ("pkv_paged_attn_decode_prefix_append" if args.prefix_shared else
                        "pkv_paged_attn_decode" if args.separate else "pkv_paged_attn_decode_append") +
-                      (" (prefix pass and suffix decode in one launch, then the finalize kernel)"
+                      (" (prefix pass and suffix decode in one launch, then the finalize kernel, which "
+                       "also writes the new rows)"
                        if args.prefix_shared else
                        f" (fixed partitions of {part} tokens: decode kernel, then a reduce when a "
                        f"sequence spans several)" if part else

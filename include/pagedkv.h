@@ -316,6 +316,41 @@ PKV_API pkv_status pkv_paged_attn_decode_prefix(void* out, const void* q,
                                         int32_t max_prefix_tokens, void* workspace,
                                         size_t workspace_bytes, void* stream);
 
+/* One prefix-shared decode step in one call: the KV append of each sequence's new token, then
+ * the decode of pkv_paged_attn_decode_prefix over contexts that include it.
+ *
+ * The new token of sequence s is its last one, position context_lens[s] - 1, in the slot its
+ * block table gives: the append step of [111cn] §3.3 after the host pool has taken that slot
+ * (pkv_seq_extend by one token, which copies a shared last block first), with the groups of
+ * pkv_pool_prefix_groups computed on the extended tables.  The result equals pkv_kv_cache_append
+ * with those slots followed by pkv_paged_attn_decode_prefix, bit for bit in the pools and in
+ * the output: the suffix pass takes each sequence's last token from new_key/new_value, and the
+ * finalize launch writes the rows to their slots after every read of the pool.  The step stays
+ * two launches.
+ *
+ *   new_key, new_value  device [num_seqs][num_kv_heads][head_dim] of cache->dtype, 16-byte
+ *                       aligned, read only
+ *   k_cache, v_cache    written at the new tokens' slots, read everywhere else
+ *   all other arguments as for pkv_paged_attn_decode_prefix
+ * Device-side contract, beyond that of pkv_paged_attn_decode_prefix: a sequence's shared prefix
+ * ends before its new token (seq_prefix[s] <= context_lens[s] - 1), as it does for groups found
+ * on tables whose last blocks are private; otherwise the prefix pass reads the slot before the
+ * write and the output is unspecified (no access outside the buffers).  Sequences with context
+ * length 0 append nothing; block ids outside the pool are skipped for the write as for the read.
+ * Errors: as pkv_paged_attn_decode_prefix, plus INVALID_ARGUMENT for missing or misaligned
+ * new_key/new_value. */
+PKV_API pkv_status pkv_paged_attn_decode_prefix_append(void* out, const void* q,
+                                               const void* new_key, const void* new_value,
+                                               void* k_cache, void* v_cache,
+                                               const pkv_cache_desc* cache,
+                                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                               const int32_t* context_lens, int32_t max_context_len,
+                                               int32_t num_seqs, int32_t num_q_heads, float scale,
+                                               const int32_t* seq_prefix, const int32_t* group_offsets,
+                                               const int32_t* group_members, int32_t num_groups,
+                                               int32_t max_prefix_tokens, void* workspace,
+                                               size_t workspace_bytes, void* stream);
+
 /* Test hook for the merge launch's bounded waits (see the status word under
  * pkv_paged_attn_workspace_bytes): sets the number of polls after which such a wait gives up,
  * for every later call in this process, and returns the previous value.  A negative limit

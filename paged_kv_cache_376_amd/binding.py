@@ -49,6 +49,8 @@ SIGNATURES = {
     "pkv_paged_attn_decode_prefix": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, ctypes.c_float,
                                             _P, _P, _P, _I32, _I32, _P, ctypes.c_size_t, _P]),
     "pkv_paged_attn_decode_prefix_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "pkv_paged_attn_decode_prefix_append": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32,
+                                                   ctypes.c_float, _P, _P, _P, _I32, _I32, _P, ctypes.c_size_t, _P]),
     "pkv_set_merge_spin_limit": (_I32, [_I32]),
     "pkv_paged_attn_decode_append_noalloc": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32,
                                                     ctypes.c_float, _I32, _P]),
@@ -331,6 +333,42 @@ def paged_attn_decode_prefix(out, q, k_cache, v_cache, block_tables, context_len
         block_tables.shape[1], _ptr(context_lens), int(max_context_len), B, Hq, float(scale), _ptr(seq_prefix),
         _ptr(group_offsets), _ptr(group_members), ng, int(max_prefix_tokens), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def paged_attn_decode_prefix_append(out, q, new_key, new_value, k_cache, v_cache, block_tables, context_lens,
+                                    max_context_len, scale, seq_prefix, group_offsets, group_members,
+                                    max_prefix_tokens, workspace=None, stream=None) -> None:
+    """pkv_paged_attn_decode_prefix_append: append new_key/new_value [B, Hkv, D] as each
+    sequence's last token, then decode with each group's shared prefix read once per group.
+    The group arrays as for paged_attn_decode_prefix (from the extended tables)."""
+    import torch
+
+    _same(out, q, k_cache, v_cache, new_key, new_value)
+    desc = cache_desc(k_cache)
+    B, Hq, D = q.shape
+    if tuple(out.shape) != (B, Hq, D) or D != desc.head_dim:
+        raise ValueError("q/out must be [B, Hq, D] with the cache's D")
+    if tuple(new_key.shape) != (B, desc.num_kv_heads, D) or tuple(new_value.shape) != tuple(new_key.shape):
+        raise ValueError("new_key/new_value must be [B, Hkv, D]")
+    for t in (block_tables, context_lens, seq_prefix, group_offsets, group_members):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("tables, lengths and group arrays must be contiguous int32")
+    if seq_prefix.numel() != B or group_offsets.numel() < 1:
+        raise ValueError("seq_prefix must have B entries, group_offsets at least one")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables must be [B, max_blocks_per_seq] and context_lens [B]")
+    _on_device(q.device, block_tables, context_lens, seq_prefix, group_offsets, group_members)
+    ng = group_offsets.numel() - 1
+    need = paged_attn_decode_prefix_workspace_bytes(B, Hq, desc.num_kv_heads, D, max_context_len, max_prefix_tokens,
+                                                    desc.dtype)
+    if workspace is None and need > 0:
+        workspace = _workspace(need, q.device, stream)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_paged_attn_decode_prefix_append(
+        _ptr(out), _ptr(q), _ptr(new_key), _ptr(new_value), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len), B, Hq, float(scale),
+        _ptr(seq_prefix), _ptr(group_offsets), _ptr(group_members), ng, int(max_prefix_tokens), _ptr(workspace),
+        ws_bytes, _stream(stream)))
 
 
 def paged_attn_decode_append(out, q, new_key, new_value, k_cache, v_cache, block_tables,

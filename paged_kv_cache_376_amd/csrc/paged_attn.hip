@@ -736,9 +736,13 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
     sp.ws_cu = cu;
     sk::PrefixParams pp{};
     pp.q = q;
-    pp.k_cache = k_cache;
-    pp.v_cache = v_cache;
+    pp.k_cache = const_cast<void*>(k_cache);  // written only with a fused append
+    pp.v_cache = const_cast<void*>(v_cache);
     pp.block_tables = block_tables;
+    pp.context_lens = context_lens;
+    pp.new_key = new_key;
+    pp.new_value = new_value;
+    pp.max_context_len = max_context_len;
     pp.seq_prefix = pre->seq_prefix;
     pp.group_offsets = pre->group_offsets;
     pp.group_members = pre->group_members;
@@ -866,6 +870,22 @@ extern "C" pkv_status pkv_paged_attn_decode_prefix(void* out, const void* q, con
   return decode_impl(out, q, k_cache, v_cache, cache, block_tables, max_blocks_per_seq, context_lens,
                      max_context_len, num_seqs, num_q_heads, scale, workspace, workspace_bytes, 0, stream, nullptr,
                      nullptr, &pre);
+}
+
+extern "C" pkv_status pkv_paged_attn_decode_prefix_append(
+    void* out, const void* q, const void* new_key, const void* new_value, void* k_cache, void* v_cache,
+    const pkv_cache_desc* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, float scale,
+    const int32_t* seq_prefix, const int32_t* group_offsets, const int32_t* group_members, int32_t num_groups,
+    int32_t max_prefix_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!new_key || !new_value) {
+    clear_error();
+    return fail(PKV_ERR_INVALID_ARGUMENT, "new_key and new_value must not be NULL");
+  }
+  const PrefixArgs pre{seq_prefix, group_offsets, group_members, num_groups, max_prefix_tokens};
+  return decode_impl(out, q, k_cache, v_cache, cache, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, num_seqs, num_q_heads, scale, workspace, workspace_bytes, 0, stream, new_key,
+                     new_value, &pre);
 }
 
 extern "C" int32_t pkv_set_merge_spin_limit(int32_t limit) {

@@ -25,9 +25,35 @@ namespace {
 // den' = den 2^(M-M') + l 2^(m-M'), and out = num / den.  The suffix's range bounds, its
 // result and the prefix partials are loaded together; only a cut suffix's records need a second
 // round of loads.  Fixed order: deterministic.
+// With a fused append, the work-group also writes its sequence's new K and V rows of its KV
+// head to the slot of the last token (position context_len - 1 through the block table; a
+// length of 0 or a block id outside the pool writes nothing), as the plain decode's merge
+// kernel does.  The launch before this one took that token from the new rows, not the pool.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void finalize_kernel(PrefixParams pp) {
   using raw = typename T::raw;
+  if (pp.new_key != nullptr) {
+    constexpr int CPR = D * static_cast<int>(sizeof(raw)) / 16;  // 16-byte chunks per row
+    const int s = blockIdx.x / pp.num_kv_heads, g = blockIdx.x % pp.num_kv_heads;
+    if (threadIdx.x < CPR) {
+      const int L0 = pp.context_lens[s];
+      const int L = L0 < 0 ? 0 : (L0 > pp.max_context_len ? pp.max_context_len : L0);
+      if (L > 0) {
+        const int phys = pp.block_tables[static_cast<int64_t>(s) * pp.max_blocks_per_seq + (L - 1) / pp.block_size];
+        if (phys >= 0 && phys < pp.num_blocks) {
+          const int64_t row_bytes = static_cast<int64_t>(D) * sizeof(raw);
+          const int ch = 16 * static_cast<int>(threadIdx.x);
+          const int64_t src = (static_cast<int64_t>(s) * pp.num_kv_heads + g) * row_bytes + ch;
+          const int64_t dst =
+              ((static_cast<int64_t>(phys) * pp.block_size + (L - 1) % pp.block_size) * pp.num_kv_heads + g) * row_bytes + ch;
+          const u32x4 kr = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(pp.new_key) + src);
+          const u32x4 vr = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(pp.new_value) + src);
+          *reinterpret_cast<u32x4*>(static_cast<unsigned char*>(pp.k_cache) + dst) = kr;
+          *reinterpret_cast<u32x4*>(static_cast<unsigned char*>(pp.v_cache) + dst) = vr;
+        }
+      }
+    }
+  }
   const int s = blockIdx.x / pp.num_kv_heads, g = blockIdx.x % pp.num_kv_heads;
   const int G = pp.group, Hkv = pp.num_kv_heads, B = pp.num_seqs;
   const int c0 = pp.cu[s], c1 = pp.cu[s + 1], ntiles = pp.cu[B], R = pp.cu[B + 1];

@@ -13,14 +13,20 @@ namespace sk {
 // (the same physical blocks) are attended once per group by the prefix pass, the rest of each
 // context by the even split in suffix and partial-result mode (both in one launch: each
 // work-group takes its prefix units first, then its range of the split), and a finalize kernel
-// merges the two (with the records of suffixes the split cut).
+// merges the two (with the records of suffixes the split cut).  With a fused append the
+// suffix pass takes each sequence's last token from the new rows, and the finalize kernel
+// writes them to their slots (the launches that read the pool are then done).
 constexpr int kPrefixChunkTiles = 32;  // 16-token tiles per prefix work-group (512 tokens)
 
 struct PrefixParams {
   const void* q;
-  const void* k_cache;
-  const void* v_cache;
+  void* k_cache;  // read by the prefix pass; written only by the finalize kernel with a fused
+  void* v_cache;  // append (new_key != NULL)
   const int32_t* block_tables;
+  const int32_t* context_lens;   // for a fused append: each sequence's last token is its new row
+  const void* new_key;           // [B][Hkv][D] or NULL: with a fused append, the finalize kernel
+  const void* new_value;         // writes each sequence's new row to its slot
+  int32_t max_context_len;
   const int32_t* seq_prefix;     // [B] shared prefix tokens of each sequence (multiple of 16), 0 if none
   const int32_t* group_offsets;  // [num_groups + 1] into group_members
   const int32_t* group_members;  // batch positions; the first member's table holds the prefix blocks
@@ -45,7 +51,8 @@ struct PrefixParams {
   float scale_log2e;
 };
 
-// Enqueues the finalize kernel (suffix results or records + prefix partials -> out).
+// Enqueues the finalize kernel (suffix results or records + prefix partials -> out; with a
+// fused append also the new rows to their slots).
 hipError_t finalize_launch(const PrefixParams& pp, int32_t dtype, hipStream_t stream);
 
 }  // namespace sk

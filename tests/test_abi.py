@@ -440,6 +440,26 @@ def test_append_rejects_before_launch():
     assert lib.pkv_kv_cache_append(16, 16, 16, 16, ctypes.byref(d), 16, 0, None) == 0
 
 
+def test_prefix_append_rejects_before_launch():
+    """The prefix-shared step with a fused append refuses missing or misaligned new rows, f32
+    pools, a missing group description and a short workspace on the host; no sequences is a
+    no-op.  No pointer is dereferenced."""
+    lib = B.lib()
+
+    def call(nk=16, nv=16, dt=2, n=2, sp=16, ws=None, wsb=0):
+        d = _desc(nb=64, hkv=2, d=128, dt=dt)
+        return lib.pkv_paged_attn_decode_prefix_append(16, 16, nk, nv, 16, 16, ctypes.byref(d), 16, 4, 16, 64, n, 4,
+                                                       ctypes.c_float(0.1), sp, 16, 16, 1, 16, ws, wsb, None)
+
+    assert call(nk=None) == 1 and b"new_key" in lib.pkv_last_error()
+    assert call(nv=None) == 1
+    assert call(nk=24) == 1                # misaligned new_key
+    assert call(dt=0) == 2                 # f32 pool: no prefix-shared path
+    assert call(sp=None) == 1              # no group description
+    assert call() == 5                     # no workspace
+    assert call(n=0) == 0
+
+
 def test_block_copies_reject_before_launch():
     lib = B.lib()
     d = _desc()

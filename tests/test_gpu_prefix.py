@@ -1,6 +1,6 @@
-"""GPU tests of the prefix-shared decode (pkv_paged_attn_decode_prefix): groups found by the
-host pool from its block tables, the shared prefix attended once per group and merged with
-each sequence's own suffix.  Parity with the attention oracle over prefix workloads, with
+"""GPU tests of the prefix-shared decode (pkv_paged_attn_decode_prefix, and with the append
+fused, pkv_paged_attn_decode_prefix_append): groups found by the host pool from its block
+tables, the shared prefix attended once per group and merged with each sequence's own suffix.  Parity with the attention oracle over prefix workloads, with
 prefixes that end inside a block or tile, empty suffixes, groups of many rows (8 members x 8
 heads), MHA groups, block sizes 8 and 32, mixed grouped and ungrouped batches, and no groups
 at all; determinism; agreement with the plain decode."""
@@ -236,6 +236,77 @@ def test_prefix_decode_full_size_every_sequence():
     assert len(offs) - 1 == 16 and mx == 1024
     assert torch.isfinite(out.float()).all()
     assert float((out.double() - plain.double()).abs().max()) <= TOL["bfloat16"]
+    ref = oracle_full(w)
+    err = np.abs(out.double().numpy() - ref).reshape(w.spec.num_seqs, -1).max(axis=1)
+    say(f"    {w.spec.num_seqs} sequences: max abs err {err.max():.3e} (sequence {int(err.argmax())})")
+    assert float(err.max()) <= TOL["bfloat16"], (float(err.max()), int(err.argmax()))
+
+
+def _prefix_decode_fused(w, fill=float("nan")):
+    """Build the pool, let the host pool take each sequence's next slot (copy-on-write copies
+    done), find the groups on the extended tables, then one pkv_paged_attn_decode_prefix_append
+    call.  Returns (out, cache, slots)."""
+    cache = build_cache(w, DEVICE, fill=fill)
+    seqs = list(range(w.spec.num_seqs))
+    slots = np.zeros(len(seqs), dtype=np.int64)
+    for i, s in enumerate(seqs):
+        sl, cow = cache.pool.seq_extend(s, 1)
+        cache.copy_blocks(cow)
+        slots[i] = sl[0]
+    bt, ctx, maxc = cache.tables(seqs)
+    sp, offs, mem, mx = cache.pool.prefix_groups(seqs, 0)
+    q = w.q.to(DEVICE).contiguous()
+    out = torch.empty_like(q)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEVICE)
+    binding.paged_attn_decode_prefix_append(out, q, w.new_k.to(DEVICE).contiguous(), w.new_v.to(DEVICE).contiguous(),
+                                            cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale, dev(sp), dev(offs),
+                                            dev(mem), mx)
+    torch.cuda.synchronize()
+    return out.cpu(), cache, slots
+
+
+FUSED_CASES = [c for c in CASES if c[0] in ("gqa-1024", "gqa-40", "gqa-nosuffix", "mha", "g16", "big-group", "bs8",
+                                           "bs32", "small-batch")]
+
+
+@pytest.mark.parametrize("name,spec", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_prefix_decode_fused_append_is_the_separate_step_bit_for_bit(name, spec):
+    """pkv_paged_attn_decode_prefix_append against pkv_kv_cache_append followed by
+    pkv_paged_attn_decode_prefix on two pools built alike: the same output bits, the same bits
+    in both whole pools (the new rows in their slots, nothing else written), and the oracle's
+    result within tolerance.  Covers suffixes that are only the new token, prefixes ending
+    inside a tile, MHA and G = 16 groups, block sizes 8 and 32 and a batch under 8."""
+    say(f"[prefix decode fused append] {name}")
+    w = W.Workload(spec, seed=41)
+    ref_out, _, _, (ref_cache, _, _, _) = _prefix_decode(w)
+    out, cache, slots = _prefix_decode_fused(w)
+    assert torch.equal(bits(out), bits(ref_out))
+    for a, b in ((cache.k_cache, ref_cache.k_cache), (cache.v_cache, ref_cache.v_cache)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    bs = spec.block_size
+    for s in range(spec.num_seqs):
+        b, o = int(slots[s]) // bs, int(slots[s]) % bs
+        assert torch.equal(cache.k_cache[b, o].cpu().view(torch.int16), w.new_k[s].view(torch.int16))
+        assert torch.equal(cache.v_cache[b, o].cpu().view(torch.int16), w.new_v[s].view(torch.int16))
+    err = max_err(out, oracle_out(w))
+    say(f"    max abs err {err:.3e}")
+    assert err <= TOL[spec.dtype]
+
+
+def test_prefix_decode_fused_append_full_size_every_sequence():
+    """The benchmark's prefix-shared step with the append fused (prefix_bf16 at full size):
+    every output of every sequence against the oracle, bit for bit the separate step's output,
+    and the new rows in their slots."""
+    say("[prefix decode fused append] full size prefix_bf16")
+    w = W.make_workload("prefix_bf16", 0)
+    ref_out, _, _, _ = _prefix_decode(w)
+    out, cache, slots = _prefix_decode_fused(w)
+    assert torch.equal(bits(out), bits(ref_out))
+    kk = cache.k_cache.view(-1, *cache.k_cache.shape[2:])
+    vv = cache.v_cache.view(-1, *cache.v_cache.shape[2:])
+    idx = torch.from_numpy(slots).to(kk.device)
+    assert torch.equal(kk[idx].cpu().view(torch.int16), w.new_k.view(torch.int16))
+    assert torch.equal(vv[idx].cpu().view(torch.int16), w.new_v.view(torch.int16))
     ref = oracle_full(w)
     err = np.abs(out.double().numpy() - ref).reshape(w.spec.num_seqs, -1).max(axis=1)
     say(f"    {w.spec.num_seqs} sequences: max abs err {err.max():.3e} (sequence {int(err.argmax())})")
