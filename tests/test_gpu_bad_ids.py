@@ -121,3 +121,47 @@ def test_out_of_pool_ids_prefix_decode():
     err = max_err(out[1:], oracle_out(w, seqs[1:]))
     say(f"    other sequences: max abs err {err:.3e}")
     assert err <= TOL["bfloat16"]
+
+
+def test_out_of_pool_ids_prefix_decode_fused_append():
+    """The prefix-shared step with the append fused, with one member's own blocks (its last
+    block too) pointing outside the pool: that member's new row goes nowhere (its slot keeps
+    the fill), every other member's new row lands in its slot, and the others' outputs match
+    the oracle."""
+    spec = W.SPECS["prefix_bf16"].replace(num_seqs=16, prefix_len=96, suffix_hi=120)
+    say("[bad ids] prefix-shared decode, append fused")
+    w = W.Workload(spec, seed=10)
+    cache = build_cache(w, DEVICE, fill=float("nan"))
+    seqs = list(range(spec.num_seqs))
+    slots = []
+    for s in seqs:
+        sl, cow = cache.pool.seq_extend(s, 1)
+        cache.copy_blocks(cow)
+        slots.append(int(sl[0]))
+    bt, ctx, maxc = cache.tables(seqs)
+    sp, offs, mem, mx = cache.pool.prefix_groups(seqs)
+    bad = bt.clone()
+    first_own = mx // spec.block_size
+    n0 = (int(ctx[0]) + spec.block_size - 1) // spec.block_size
+    assert n0 - 1 >= first_own  # the last block, which holds the new token, is one of them
+    for i in range(first_own, n0):
+        bad[0, i] = -3 if i % 2 else w.num_blocks + i
+    q = w.q.to(DEVICE).contiguous()
+    out = torch.empty_like(q)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEVICE)
+    binding.paged_attn_decode_prefix_append(out, q, w.new_k.to(DEVICE).contiguous(), w.new_v.to(DEVICE).contiguous(),
+                                            cache.k_cache, cache.v_cache, bad, ctx, maxc, w.scale,
+                                            dev(sp), dev(offs), dev(mem), mx)
+    torch.cuda.synchronize()
+    out = out.cpu()
+    assert torch.isfinite(out[0].float()).all()
+    err = max_err(out[1:], oracle_out(w, seqs[1:]))
+    say(f"    other sequences: max abs err {err:.3e}")
+    assert err <= TOL["bfloat16"]
+    bs = spec.block_size
+    for i in seqs[1:]:
+        b, o = slots[i] // bs, slots[i] % bs
+        assert torch.equal(cache.k_cache[b, o].cpu().view(torch.int16), w.new_k[i].view(torch.int16))
+        assert torch.equal(cache.v_cache[b, o].cpu().view(torch.int16), w.new_v[i].view(torch.int16))
+    b0, o0 = slots[0] // bs, slots[0] % bs
+    assert torch.isnan(cache.k_cache[b0, o0].float()).all() and torch.isnan(cache.v_cache[b0, o0].float()).all()

@@ -65,12 +65,23 @@ def test_fused_decode_step_in_a_graph(name):
     _replay_and_check(g, out, expect)
 
 
-def test_prefix_decode_in_a_graph():
-    say("[graph] prefix-shared decode")
+@pytest.mark.parametrize("fused", [False, True])
+def test_prefix_decode_in_a_graph(fused):
+    """The prefix-shared decode, and with fused=True the prefix-shared step with its append
+    (pkv_paged_attn_decode_prefix_append), captured once; with the append fused, the new-token
+    slots are cleared before every replay and must hold the new rows after it."""
+    say(f"[graph] prefix-shared decode (append fused: {fused})")
     w = W.Workload(W.SPECS["prefix_bf16"].replace(num_seqs=16, suffix_hi=200), seed=4)
     cache = build_cache(w, DEVICE, fill=float("nan"))
     seqs = list(range(w.spec.num_seqs))
-    cache.append_tokens(seqs, w.new_k, w.new_v)
+    if fused:
+        slots = []
+        for s_ in seqs:
+            sl, cow = cache.pool.seq_extend(s_, 1)
+            cache.copy_blocks(cow)
+            slots.append(int(sl[0]))
+    else:
+        cache.append_tokens(seqs, w.new_k, w.new_v)
     bt, ctx, maxc = cache.tables(seqs)
     spf, offs, mem, mx = cache.pool.prefix_groups(seqs)
     d32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEVICE)
@@ -81,8 +92,13 @@ def test_prefix_decode_in_a_graph():
                      dtype=torch.uint8, device=DEVICE)
     q = w.q.to(DEVICE)
     out = torch.empty_like(q)
-    call = lambda: binding.paged_attn_decode_prefix(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale,
-                                                    spd, offd, memd, mx, workspace=ws)
+    nk, nv = w.new_k.to(DEVICE), w.new_v.to(DEVICE)
+    if fused:
+        call = lambda: binding.paged_attn_decode_prefix_append(out, q, nk, nv, cache.k_cache, cache.v_cache, bt, ctx,
+                                                               maxc, w.scale, spd, offd, memd, mx, workspace=ws)
+    else:
+        call = lambda: binding.paged_attn_decode_prefix(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale,
+                                                        spd, offd, memd, mx, workspace=ws)
     call()
     torch.cuda.synchronize()
     expect = out.cpu()
@@ -95,7 +111,22 @@ def test_prefix_decode_in_a_graph():
             call()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    _replay_and_check(g, out, expect)
+    if not fused:
+        _replay_and_check(g, out, expect)
+        return
+    kf = cache.k_cache.view(-1, *cache.k_cache.shape[2:])
+    vf = cache.v_cache.view(-1, *cache.v_cache.shape[2:])
+    idx = torch.tensor(slots, dtype=torch.int64, device=DEVICE)
+    for i in range(4):
+        kf[idx] = float("nan")
+        vf[idx] = float("nan")
+        out.fill_(float("nan"))
+        _eager_noise()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(out.cpu()), bits(expect)), f"replay {i}"
+        assert torch.equal(bits(kf[idx].cpu()), bits(w.new_k)) and torch.equal(bits(vf[idx].cpu()), bits(w.new_v)), \
+            f"replay {i}"
 
 
 def test_append_and_copy_in_a_graph():

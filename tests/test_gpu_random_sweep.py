@@ -105,25 +105,51 @@ def test_random_prefix_decode_partial_head_groups(seed):
     _check_prefix(100 + seed, *_draw_prefix(3000 + seed, hkv_choices=(3, 5, 6, 7)))
 
 
-def _check_prefix(seed, spec, min_prefix):
+@pytest.mark.parametrize("seed", range(8))
+def test_random_prefix_decode_fused_append_matches_oracle(seed):
+    """pkv_paged_attn_decode_prefix_append on random shapes: the shuffled batch's sequences
+    take their next slots, groups are found on the extended tables, one call appends and
+    decodes; every output against the oracle and every new row in its slot bit for bit."""
+    _check_prefix(300 + seed, *_draw_prefix(4000 + seed), fused=True)
+
+
+def _check_prefix(seed, spec, min_prefix, fused=False):
     say(f"[random prefix] seed {seed}: {spec.dtype} D={spec.head_dim} Hkv={spec.num_kv_heads} "
         f"G={spec.num_q_heads // spec.num_kv_heads} groups of {spec.group_size} x {spec.num_seqs // spec.group_size} "
         f"prefix={spec.prefix_len} suffix<= {spec.suffix_hi} bs={spec.block_size} min_prefix={min_prefix}")
     w = W.Workload(spec, seed=seed)
     cache = build_cache(w, DEVICE, fill=float("nan"))
     seqs = list(range(spec.num_seqs))
-    cache.append_tokens(seqs, w.new_k, w.new_v)
     # a shuffled batch, with one sequence left out when there are several
     order = list(np.random.default_rng(seed).permutation(spec.num_seqs))
-    batch = order[:-1] if len(order) > 2 else order
+    batch = [int(x) for x in (order[:-1] if len(order) > 2 else order)]
+    if fused:  # only the batch's sequences take a slot; the call writes their rows
+        slots = []
+        for s in batch:
+            sl, cow = cache.pool.seq_extend(s, 1)
+            cache.copy_blocks(cow)
+            slots.append(int(sl[0]))
+    else:
+        cache.append_tokens(seqs, w.new_k, w.new_v)
     bt, ctx, maxc = cache.tables(batch)
     sp, offs, mem, mx = cache.pool.prefix_groups(batch, min_prefix)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEVICE)
     q = w.q[batch].to(DEVICE).contiguous()
     out = torch.empty_like(q)
-    binding.paged_attn_decode_prefix(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale,
-                                     dev(sp), dev(offs), dev(mem), mx)
+    if fused:
+        binding.paged_attn_decode_prefix_append(out, q, w.new_k[batch].to(DEVICE).contiguous(),
+                                                w.new_v[batch].to(DEVICE).contiguous(), cache.k_cache, cache.v_cache,
+                                                bt, ctx, maxc, w.scale, dev(sp), dev(offs), dev(mem), mx)
+    else:
+        binding.paged_attn_decode_prefix(out, q, cache.k_cache, cache.v_cache, bt, ctx, maxc, w.scale,
+                                         dev(sp), dev(offs), dev(mem), mx)
     torch.cuda.synchronize()
+    if fused:
+        bs = spec.block_size
+        for i, s in enumerate(batch):
+            b, o = slots[i] // bs, slots[i] % bs
+            assert torch.equal(cache.k_cache[b, o].cpu().view(torch.int16), w.new_k[s].view(torch.int16))
+            assert torch.equal(cache.v_cache[b, o].cpu().view(torch.int16), w.new_v[s].view(torch.int16))
     err = max_err(out.cpu(), oracle_out(w, batch))
     say(f"    groups {len(offs) - 1}, longest shared prefix {mx}: max abs err {err:.3e}")
     assert torch.isfinite(out.float()).all()
