@@ -211,10 +211,12 @@ PKV_API pkv_status pkv_paged_attn_decode(void* out, const void* q,
  * block table gives (block block_tables[s][(ctx-1)/bs], offset (ctx-1) % bs): the append step
  * of [111cn] §3.3 after the host pool has taken that slot (pkv_seq_extend by one token).
  * The result equals pkv_kv_cache_append with those slots followed by pkv_paged_attn_decode,
- * bit for bit in the pools and in the output.  On the evenly split path the wave that
- * reads a sequence's last tile takes the new row from new_key/new_value, and the merge
- * launch that follows the decode writes the rows to their slots, so the step is the decode
- * launch plus the merge; otherwise a scatter launch precedes the decode.
+ * bit for bit in the pools and in the output.  The wave that reads a sequence's last tile
+ * takes the new row from new_key/new_value.  On the evenly split path the merge launch that
+ * follows the decode writes the rows to their slots, so the step is the decode launch plus
+ * the merge; with fixed partitions the work-group of each sequence's last partition writes
+ * its KV head's row, so the step is the decode launch (plus the reduce when a sequence spans
+ * several partitions).
  *
  *   new_key, new_value  device [num_seqs][num_kv_heads][head_dim] of cache->dtype, 16-byte
  *                       aligned, read only

@@ -15,7 +15,6 @@
 // before any pool address is formed.
 #include <hip/hip_runtime.h>
 
-#include "device_launch.h"
 #include "pkv_internal.h"
 
 namespace {
@@ -53,68 +52,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint4* __restrict_
   }
 }
 
-// One work-group per sequence: the sequence's new token is its last one (position
-// context_lens[s] - 1), whose slot the block table gives.  Empty contexts and block ids
-// outside the pool are skipped.
-__global__ __launch_bounds__(256) void kv_append_last_kernel(const uint4* __restrict__ key,
-                                                             const uint4* __restrict__ value,
-                                                             uint4* __restrict__ k_cache,
-                                                             uint4* __restrict__ v_cache,
-                                                             const int32_t* __restrict__ block_tables,
-                                                             int32_t max_blocks_per_seq,
-                                                             const int32_t* __restrict__ context_lens,
-                                                             int32_t max_context_len, int32_t num_blocks,
-                                                             int32_t block_size, int32_t row_vecs) {
-  const int64_t s = blockIdx.x;
-  const uint4* ks = key + s * row_vecs;
-  const uint4* vs = value + s * row_vecs;
-  // the row's first piece is loaded while the context length and table entry are fetched
-  const int32_t i0 = threadIdx.x;
-  uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
-  if (i0 < row_vecs) {
-    a = ks[i0];
-    b = vs[i0];
-  }
-  int ctx = context_lens[s];
-  ctx = ctx > max_context_len ? max_context_len : ctx;
-  if (ctx <= 0) return;
-  const int t = ctx - 1;
-  const int phys = block_tables[s * max_blocks_per_seq + t / block_size];
-  if (phys < 0 || phys >= num_blocks) return;
-  const int64_t slot = static_cast<int64_t>(phys) * block_size + t % block_size;
-  uint4* kd = k_cache + slot * row_vecs;
-  uint4* vd = v_cache + slot * row_vecs;
-  if (i0 < row_vecs) {
-    kd[i0] = a;
-    vd[i0] = b;
-  }
-  for (int32_t i = i0 + blockDim.x; i < row_vecs; i += blockDim.x) {
-    const uint4 c = ks[i];
-    const uint4 d = vs[i];
-    kd[i] = c;
-    vd[i] = d;
-  }
-}
-
 }  // namespace
-
-namespace pkv {
-
-hipError_t launch_append_last(const void* key, const void* value, void* k_cache, void* v_cache,
-                              const pkv_cache_desc* cache, const int32_t* block_tables,
-                              int32_t max_blocks_per_seq, const int32_t* context_lens,
-                              int32_t max_context_len, int32_t num_seqs, hipStream_t stream) {
-  const int32_t row_vecs = cache->num_kv_heads * cache->head_dim * dtype_bytes(cache->dtype) / 16;
-  const int threads = row_vecs >= 256 ? 256 : ((row_vecs + 63) / 64) * 64;
-  hipLaunchKernelGGL(kv_append_last_kernel, dim3(num_seqs), dim3(threads), 0, stream,
-                     static_cast<const uint4*>(key), static_cast<const uint4*>(value),
-                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), block_tables,
-                     max_blocks_per_seq, context_lens, max_context_len, cache->num_blocks,
-                     cache->block_size, row_vecs);
-  return hipGetLastError();
-}
-
-}  // namespace pkv
 
 extern "C" pkv_status pkv_kv_cache_append(const void* key, const void* value, void* k_cache,
                                           void* v_cache, const pkv_cache_desc* cache,

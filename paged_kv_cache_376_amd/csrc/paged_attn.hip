@@ -41,7 +41,6 @@
 #include <mutex>
 #include <type_traits>
 
-#include "device_launch.h"
 #include "dtypes.h"
 #include "pkv_internal.h"
 #include "prefix.h"
@@ -59,10 +58,12 @@ constexpr float kNegBig = -1.0e30f;  // finite start value for the running max
 struct Params {
   void* out;
   const void* q;
-  const void* k_cache;
-  const void* v_cache;
+  void* k_cache;  // written only with a fused append (new_key != NULL): the new rows
+  void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const void* new_key;    // [B][Hkv][D] or NULL: with a fused append, each sequence's last token
+  const void* new_value;  // comes from here (write_new_row puts it in its slot)
   float* ws_acc;  // [B][Hq][P][D]
   float* ws_ml;   // [B][Hq][P][2]  (m, l)
   int32_t num_seqs;
@@ -88,6 +89,25 @@ __device__ __forceinline__ int clamped_ctx(const Params& p, int s) {
   int ctx = p.context_lens[s];
   ctx = ctx < 0 ? 0 : ctx;
   return ctx > p.max_context_len ? p.max_context_len : ctx;
+}
+
+// Fused append: the work-group of a sequence's last partition writes the new K and V rows of
+// its KV head to the slot of the sequence's last token (position ctx - 1 through the block
+// table; an empty context or a block id outside the pool writes nothing).  The loads of that
+// block take the token's row from new_key / new_value instead of the slot, so nothing in the
+// launch reads what this writes.
+template <typename T, int D>
+__device__ __forceinline__ void write_new_row(const Params& p, int s, int g, int ctx) {
+  constexpr int CPR = D * T::kBytes / 16;  // 16-byte chunks per row
+  if (ctx <= 0 || static_cast<int>(threadIdx.x) >= 2 * CPR) return;
+  const int phys = p.block_tables[static_cast<int64_t>(s) * p.max_blocks_per_seq + (ctx - 1) / kBlock];
+  if (phys < 0 || phys >= p.num_blocks) return;
+  const int which = threadIdx.x / CPR, ch = threadIdx.x % CPR;
+  const int64_t src = (static_cast<int64_t>(s) * p.num_kv_heads + g) * CPR + ch;
+  const int64_t dst =
+      ((static_cast<int64_t>(phys) * kBlock + (ctx - 1) % kBlock) * p.num_kv_heads + g) * CPR + ch;
+  const u32x4 x = static_cast<const u32x4*>(which ? p.new_value : p.new_key)[src];
+  static_cast<u32x4*>(which ? p.v_cache : p.k_cache)[dst] = x;
 }
 
 __device__ __forceinline__ int num_parts_of(int ctx, int part_blocks) {
@@ -134,10 +154,13 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(Params p) {
   if (part >= nparts) return;
   const int b_begin = part * p.part_blocks;
   const int b_end = min(nblk, b_begin + p.part_blocks);
+  const bool append = p.new_key != nullptr;
+  if (append && part == nparts - 1) write_new_row<T, D>(p, s, g, ctx);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tok = lane >> 2, quad = lane & 3;
   const int Hkv = p.num_kv_heads;
+  const int64_t new_row = (static_cast<int64_t>(s) * Hkv + g) * D;  // this head's new row (fused append)
 
   // Query rows of the G heads, pre-scaled into the log2 domain.  Lane element (c, e) is
   // d = (quad + 4c) * E + e -- the same split the K/V rows use below.
@@ -178,8 +201,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(Params p) {
     if (phys < 0 || phys >= p.num_blocks) return false;
     const int64_t off = (static_cast<int64_t>(phys) * kBlock + tok) * tok_stride +
                         static_cast<int64_t>(g) * D;
-    const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + off);
-    const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + off);
+    // with a fused append, the lanes of the last token's row read it from the input
+    const bool mine = append && blk == nblk - 1 && tok == (ctx - 1) % kBlock;
+    const u32x4* kp = reinterpret_cast<const u32x4*>(mine ? static_cast<const raw*>(p.new_key) + new_row : kbase + off);
+    const u32x4* vp = reinterpret_cast<const u32x4*>(mine ? static_cast<const raw*>(p.new_value) + new_row : vbase + off);
 #pragma unroll
     for (int c = 0; c < VPL; ++c) {
       kr[c] = kp[quad + 4 * c];
@@ -316,6 +341,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
   if (part >= nparts) return;
   const int b_begin = part * p.part_blocks;
   const int b_end = min(nblk, b_begin + p.part_blocks);
+  const bool append = p.new_key != nullptr;
+  if (append && part == nparts - 1) write_new_row<T, D>(p, s, g, ctx);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15;  // MFMA row/column index of this lane
@@ -364,8 +391,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
     const int phys = bt[blk];
     if (phys < 0 || phys >= p.num_blocks) return false;
     const int64_t blk_off = static_cast<int64_t>(phys) * kBlock * tok_bytes + static_cast<int64_t>(g) * ROW_BYTES;
-    const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + blk_off + r16 * tok_bytes);
-    const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + blk_off + vt * tok_bytes);
+    // with a fused append, the lanes of the last token's row read it from the input
+    const bool last = append && blk == nblk - 1;
+    const int lt = (ctx - 1) % kBlock;
+    const int64_t new_off = (static_cast<int64_t>(s) * Hkv + g) * ROW_BYTES;
+    const u32x4* kp = reinterpret_cast<const u32x4*>(
+        last && r16 == lt ? static_cast<const unsigned char*>(p.new_key) + new_off : kbase + blk_off + r16 * tok_bytes);
+    const u32x4* vp = reinterpret_cast<const u32x4*>(
+        last && vt == lt ? static_cast<const unsigned char*>(p.new_value) + new_off : vbase + blk_off + vt * tok_bytes);
 #pragma unroll
     for (int c = 0; c < KC; ++c) kr[c] = kp[grp + 4 * c];
 #pragma unroll
@@ -619,8 +652,10 @@ size_t prefix_extra_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_di
 }
 
 // Shared body of the decode entry points.  With new_key/new_value set, each sequence's
-// last token first gets its new K/V row (inside the decode kernel on the evenly split path,
-// by a separate scatter launch otherwise).
+// last token is its new K/V row: the decode kernels read it from the input, and a later kernel
+// of the same call (the merge kernel of the even split, the finalize kernel of the prefix-shared
+// decode) or the last partition's work-group of the fixed-partition decode writes it to its
+// slot.
 pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                        const pkv_cache_desc* cache, const int32_t* block_tables,
                        int32_t max_blocks_per_seq, const int32_t* context_lens,
@@ -784,10 +819,12 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
   Params p;
   p.out = out;
   p.q = q;
-  p.k_cache = k_cache;
-  p.v_cache = v_cache;
+  p.k_cache = const_cast<void*>(k_cache);  // written only with a fused append
+  p.v_cache = const_cast<void*>(v_cache);
   p.block_tables = block_tables;
   p.context_lens = context_lens;
+  p.new_key = new_key;
+  p.new_value = new_value;
   p.ws_acc = static_cast<float*>(workspace);
   p.ws_ml = need > 0 ? p.ws_acc + static_cast<size_t>(num_seqs) * num_q_heads * P * D : nullptr;
   p.num_seqs = num_seqs;
@@ -802,11 +839,6 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
-  if (append) {
-    err = launch_append_last(new_key, new_value, const_cast<void*>(k_cache), const_cast<void*>(v_cache), cache,
-                             block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs, st);
-    if (err != hipSuccess) return fail(PKV_ERR_HIP, "append launch: %s", hipGetErrorString(err));
-  }
   switch (cache->dtype) {
     case PKV_F32: err = launch_dtype<F32>(p, D, G, st); break;
     case PKV_F16: err = launch_dtype<F16>(p, D, G, st); break;

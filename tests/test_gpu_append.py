@@ -90,6 +90,11 @@ FUSED = [
     (W.Spec("f16g4d64", "float16", 6, 16, 4, 64, "fixed", fixed_lengths=(15, 16, 31, 200, 1, 600)), 0),
     (W.SPECS["mha_fp16"].replace(num_seqs=5, len_lo=100, len_hi=400), 0),
     (W.SPECS["tiny_fp32"], 0),
+    # fixed partitions with the append fused into the decode kernels: f32 with G = 2 and D 128
+    # (new tokens that open a block, a two-partition sequence), f16 with G = 1 and explicit
+    # 32-token partitions
+    (W.Spec("f32g2", "float32", 5, 8, 4, 128, "fixed", fixed_lengths=(16, 1, 33, 700, 64)), 0),
+    (W.Spec("f16g1p32", "float16", 4, 4, 4, 64, "fixed", fixed_lengths=(15, 47, 300, 2)), 32),
     # prefix groups whose shared prefix ends inside a block: copy-on-write before the append
     (W.SPECS["prefix_bf16"].replace(num_seqs=16, prefix_len=40, suffix_hi=30), 0),
 ]
