@@ -268,6 +268,19 @@ __device__ __forceinline__ void decode_sk_body(const SkParams& p, int bid, unsig
   const int t1 = T0 + static_cast<int>(static_cast<int64_t>(T1 - T0) * (sw + 1) / kSplits);
   const int n = head_ok ? t1 - t0 : 0;
 
+  // Writes a record of this work-group's range for KV head g (rows r16 < G): slot 0 holds a
+  // sequence that began before the range, slot 1 one that began inside it and runs past it.
+  auto store_record = [&](int slot, float rm, float rl, const f32x4* ra) {
+    const int64_t rec = (static_cast<int64_t>(wgr) * p.num_kv_heads + g) * 2 + slot;
+    float* pa = p.ws_acc + rec * (16 * D) + r16 * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) __builtin_nontemporal_store(ra[c], reinterpret_cast<f32x4*>(pa + 16 * c + 4 * grp));
+    if (grp == 0) {
+      __builtin_nontemporal_store(rm, p.ws_ml + rec * 32 + r16 * 2);
+      __builtin_nontemporal_store(rl, p.ws_ml + rec * 32 + r16 * 2 + 1);
+    }
+  };
+
   // state of the segment that began before this wave (A) and of the one that runs past its end (Z)
   bool hasA = false, a_through = false, hasZ = false;
   int sA = -1, sZ = -1;
@@ -535,6 +548,19 @@ __device__ __forceinline__ void decode_sk_body(const SkParams& p, int bid, unsig
     }
   }
 
+  // Records that no other wave of the work-group joins go out now rather than after its
+  // barriers (none inside the tile loop: there a store would hold up the next tile's loads, as
+  // loads and stores share one counter): a sequence that began before the range and ends in
+  // its first sub-range (slot 0), one that began in its last sub-range and runs past it (slot 1).
+  if (sw == 0 && hasA && !a_through) {
+    if (head_ok && r16 < G) store_record(0, mA, lA, accA);
+    hasA = false;
+  }
+  if (sw == kSplits - 1 && hasZ) {
+    if (head_ok && r16 < G) store_record(1, m_run, lZ, acc);
+    hasZ = false;
+  }
+
   // ---- merge what crosses the sub-ranges of this work-group; hand the rest to the merge kernel
   __syncthreads();  // every wave is done with its V tile: the region now holds wave states
   const int sb = sk_state_bytes(D, G);
@@ -564,6 +590,8 @@ __device__ __forceinline__ void decode_sk_body(const SkParams& p, int bid, unsig
   // Walk the sub-ranges of head column hw in order.  A chain is a sequence cut by sub-range boundaries; it is
   // finished here when it starts and ends inside the work-group, and otherwise leaves one
   // record: slot 0 if it began before this work-group's range, slot 1 if it only runs past it.
+  // A sequence that lies in the first sub-range alone and began before the range, or in the
+  // last sub-range alone and runs past it, left its record from its own wave already.
   bool open = false, before = false;
   float cm = kNegBig, cl = 0.f;
   f32x4 ca[NC];
@@ -584,16 +612,7 @@ __device__ __forceinline__ void decode_sk_body(const SkParams& p, int bid, unsig
 #pragma unroll
     for (int c = 0; c < NC; ++c) ca[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
-  auto record = [&](int slot) {
-    const int64_t rec = (static_cast<int64_t>(wgr) * p.num_kv_heads + g) * 2 + slot;
-    float* pa = p.ws_acc + rec * (16 * D) + r16 * D;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) __builtin_nontemporal_store(ca[c], reinterpret_cast<f32x4*>(pa + 16 * c + 4 * grp));
-    if (grp == 0) {
-      __builtin_nontemporal_store(cm, p.ws_ml + rec * 32 + r16 * 2);
-      __builtin_nontemporal_store(cl, p.ws_ml + rec * 32 + r16 * 2 + 1);
-    }
-  };
+  auto record = [&](int slot) { store_record(slot, cm, cl, ca); };
   for (int sp = 0; sp < kSplits; ++sp) {
     const int w = sp * kHeads + hw;
     if (s_flags[w][0]) {
