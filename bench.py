@@ -69,11 +69,13 @@ def prefix_shared_bytes(w, seq_prefix, group_offsets, group_members):
 _CSRC = os.path.join(ROOT, "paged_kv_cache_376_amd", "csrc")
 SK_SOURCES = [os.path.join(_CSRC, f) for f in ("paged_attn_sk.hip", "tile_common.h", "stream_k.h", "dtypes.h")]
 PREFIX_SOURCES = SK_SOURCES + [os.path.join(_CSRC, f) for f in ("paged_attn_prefix.hip", "prefix.h", "prefix_body.h")]
+FIXED_SOURCES = [os.path.join(_CSRC, f) for f in ("paged_attn.hip", "dtypes.h")]
 COUNTER_FILES = {
     ("gqa_bf16", "fused"): ("decode_gqa_bf16_B256_counters.md", SK_SOURCES),
     ("mha_fp16", "fused"): ("decode_mha_fp16_B64_counters.md", SK_SOURCES),
     ("long_bf16", "fused"): ("decode_long_bf16_B8_counters.md", SK_SOURCES),
     ("prefix_bf16", "fused"): ("decode_prefix_bf16_B128_counters.md", SK_SOURCES),
+    ("tiny_fp32", "fused"): ("decode_tiny_fp32_B4_counters.md", FIXED_SOURCES),
     ("prefix_bf16", "prefix"): ("decode_prefix_bf16_B128_shared_counters.md", PREFIX_SOURCES),
 }
 
