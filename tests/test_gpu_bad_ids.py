@@ -57,11 +57,19 @@ def test_out_of_pool_ids_are_skipped(name, spec, partition):
     assert err <= TOL[spec.dtype]
 
 
-def test_out_of_pool_ids_fused_append():
+FUSED_CASES = [
+    ("even", W.SPECS["gqa_bf16"].replace(num_seqs=5, len_hi=400), 0),
+    ("fixed-64", W.SPECS["gqa_bf16"].replace(num_seqs=5, len_hi=400), 64),  # matrix kernel, fixed partitions
+    ("fp32", W.SPECS["tiny_fp32"], 0),                                      # vector kernel, fixed partitions
+]
+
+
+@pytest.mark.parametrize("name,spec,partition", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_out_of_pool_ids_fused_append(name, spec, partition):
     """The fused call: a damaged table must not make the append write outside the pool, and the
-    other sequences' new rows still land in their slots."""
-    spec = W.SPECS["gqa_bf16"].replace(num_seqs=5, len_hi=400)
-    say("[bad ids] fused append")
+    other sequences' new rows still land in their slots.  On the even split the merge kernel
+    writes the rows, on the fixed-partition path the decode kernels themselves."""
+    say(f"[bad ids] fused append {name}")
     w = W.Workload(spec, seed=8)
     cache = build_cache(w, DEVICE, fill=float("nan"))
     seqs = list(range(spec.num_seqs))
@@ -79,20 +87,22 @@ def test_out_of_pool_ids_fused_append():
     q = w.q.to(DEVICE).contiguous()
     out = torch.empty_like(q)
     binding.paged_attn_decode_append(out, q, w.new_k.to(DEVICE).contiguous(), w.new_v.to(DEVICE).contiguous(),
-                                     cache.k_cache, cache.v_cache, bad, ctx, maxc, w.scale)
+                                     cache.k_cache, cache.v_cache, bad, ctx, maxc, w.scale, partition_size=partition)
     torch.cuda.synchronize()
     out = out.cpu()
     assert torch.isfinite(out[0].float()).all()
     err = max_err(out[1:], oracle_out(w, seqs[1:]))
     say(f"    other sequences: max abs err {err:.3e}")
-    assert err <= TOL["bfloat16"]
+    assert err <= TOL[spec.dtype]
     bs = spec.block_size
+    view = {4: torch.int32, 2: torch.int16}[cache.k_cache.element_size()]
     for i in seqs[1:]:
         b, o = slots[i] // bs, slots[i] % bs
-        assert torch.equal(cache.k_cache[b, o].cpu().view(torch.int16), w.new_k[i].view(torch.int16))
+        assert torch.equal(cache.k_cache[b, o].cpu().view(view), w.new_k[i].view(view))
+        assert torch.equal(cache.v_cache[b, o].cpu().view(view), w.new_v[i].view(view))
     # sequence 0's slot was not written (it still holds the NaN fill)
     b0, o0 = slots[0] // bs, slots[0] % bs
-    assert torch.isnan(cache.k_cache[b0, o0].float()).all()
+    assert torch.isnan(cache.k_cache[b0, o0].float()).all() and torch.isnan(cache.v_cache[b0, o0].float()).all()
 
 
 def test_out_of_pool_ids_prefix_decode():
