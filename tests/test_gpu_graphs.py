@@ -31,10 +31,14 @@ def _replay_and_check(graph, out, expect, replays=4):
         assert torch.equal(bits(out.cpu()), bits(expect)), f"replay {i}"
 
 
-@pytest.mark.parametrize("name", ["gqa_bf16", "mha_fp16"])
+@pytest.mark.parametrize("name", ["gqa_bf16", "mha_fp16", "tiny_fp32"])
 def test_fused_decode_step_in_a_graph(name):
+    """The fused decode step captured once and replayed: on the even split (gqa_bf16, mha_fp16)
+    and on the fixed-partition path (tiny_fp32, fp32), where the decode kernels write the new
+    rows themselves."""
     say(f"[graph] fused decode step {name}")
-    overrides = {"gqa_bf16": {"num_seqs": 24, "len_hi": 2000}, "mha_fp16": {"num_seqs": 8, "len_hi": 900}}[name]
+    overrides = {"gqa_bf16": {"num_seqs": 24, "len_hi": 2000}, "mha_fp16": {"num_seqs": 8, "len_hi": 900},
+                 "tiny_fp32": {}}[name]
     w = W.make_workload(name, 3, **overrides)
     cache = build_cache(w, DEVICE, fill=float("nan"))
     seqs = list(range(w.spec.num_seqs))
